@@ -1,0 +1,261 @@
+#!/usr/bin/env python3
+"""Benchmark of the QLoRA NF4 + double-quant linear layer on one MI355X.
+
+One step = one pass of the whole hot path over one batch of seeded synthetic
+input, with every input already resident in HBM:
+  blockwise NF4 + double quantization of the fp32 weight,
+  forward  Y = X·Ŵ + s·(X·A)·B   (T = X·A kept for the backward),
+  backward dX = dY·Ŵᵀ + s·(dY·Bᵀ)·Aᵀ, dA, dB.
+Default workload: one 4096×4096 linear, 4096 tokens (2 × 2048), rank 64,
+s = 2, W ~ N(0, 0.02), X, dY ~ N(0, 1), A, B ~ N(0, 0.02).
+
+`value` is algorithmic fwd+bwd TFLOP/s, 4·M·d·o + 6·M·r·(d+o) FLOP per step
+(quantize and dequant count no FLOPs; their time is included).  The JSON line
+also carries the dominant kernel's roofline, the few-token dequant-GEMV
+bandwidth on the 7B-style MLP weights, and the CPU oracle timed on the host.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
+PROFILE_PMC = os.path.join(ROOT, "profiles", "pmc_main_gemm_linear_4096.json")
+KERNEL_SOURCES = ["gemm.hip", "kernels.h", "common.h"]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="linear_4096")
+    ap.add_argument("--decode-sets", type=int, default=16,
+                    help="independent weight sets cycled by the decode measurement")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "nf4_double_quant_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def step_flops(M, d, o, r):
+    return 4 * M * d * o + 6 * M * r * (d + o)
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the layer would shard by tokens with an all-reduce of dA, dB; not built).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import nf4_double_quant_amd as qb
+    import synth
+
+    qb.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = synth.WORKLOADS[args.workload]
+    p = wl.projs[0]
+    M, d, o, r, s = wl.M, p.d, p.o, wl.r, wl.s
+
+    W_h, X_h, A_h, B_h, dY_h = synth.layer_inputs(wl, p)
+    bf = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
+    W = torch.from_numpy(W_h).to(dev)
+    X, A, B, dY = bf(X_h), bf(A_h), bf(B_h), bf(dY_h)
+    q = qb.qlora_quantize_nf4_dq(W)
+    Y = torch.empty((M, o), dtype=torch.bfloat16, device=dev)
+    ws_f, ws_b = qb.Workspace(), qb.Workspace()
+
+    def step():
+        qb.qlora_quantize_nf4_dq(W, check_finite=False, out=q)
+        _, T = qb.qlora_linear_fwd(X, q, A, B, s, ws=ws_f, out=Y)
+        qb.qlora_linear_bwd(dY, X, T, q, A, B, s, ws=ws_b)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    qb.qlora_timing_begin()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    qb.qlora_timing_end()
+    ms_step = e0.elapsed_time(e1) / args.steps
+    wall_ms_step = (t1 - t0) * 1e3 / args.steps
+    per_class = {name: qb.qlora_timing_read(k) for name, k in qb.KERNEL_CLASSES.items()}
+
+    flops = step_flops(M, d, o, r)
+    value = flops / (ms_step * 1e-3) / 1e12
+
+    # dominant kernel: the fused main product (forward Y and backward dX)
+    gemm_ms, gemm_n = per_class["main_gemm"]
+    gemm_flop_per_launch = (2 * M * d * o + 2 * M * r * o + 2 * M * o * d + 2 * M * r * d) / 2
+    gemm_avg_ms = gemm_ms / max(gemm_n, 1)
+    achieved = gemm_flop_per_launch / (gemm_avg_ms * 1e-3) / 1e12
+    traffic = None
+    if os.path.exists(PROFILE_PMC):
+        with open(PROFILE_PMC) as f:
+            pmc = json.load(f)
+        if pmc.get("kernel_source_hash") == kernel_source_hash() and pmc.get("workload") == wl.name:
+            traffic = pmc.get("hbm_bytes_per_launch")
+    roofline = {"bound": "mfma", "kernel": "k_gemm 256x256 (Y = X·Ŵ + sT·B and dX = dY·Ŵᵀ + sU·Aᵀ)",
+                "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                "flop_per_launch": gemm_flop_per_launch, "avg_launch_us": round(gemm_avg_ms * 1e3, 2),
+                "launches": gemm_n}
+
+    breakdown = {name: {"ms_per_step": round(ms / args.steps, 4), "launches_per_step": n / args.steps}
+                 for name, (ms, n) in per_class.items() if n}
+
+    decode = None if args.no_decode else bench_decode(args, qb, torch, np, synth, dev)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args, wl, p)
+
+    out = {
+        "metric": "QLoRA linear fwd+bwd TFLOP/s (4096 tok) and dequant-GEMV GB/s vs HBM peak",
+        "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "wall_ms_per_step": round(wall_ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded Gaussian, random-init; no datasets or trained weights)",
+        "config": {"workload": wl.name, "M": M, "d": d, "o": o, "r": r, "s": s, "w_std": wl.w_std,
+                   "step": "quantize NF4+DQ + fwd + bwd (dX, dA, dB)", "flop_per_step": flops,
+                   "parallelism": "single GPU"},
+        "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "roofline": roofline, "breakdown": breakdown, "decode": decode, "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def bench_decode(args, qb, torch, np, synth, dev):
+    """Few-token forward on 7B-style gate/up/down NF4 weights, rank 16, cycling
+    independent weight sets so the 256 MB MALL cannot hold them."""
+    wl = synth.WORKLOADS["decode_mlp_7b"]
+    # weight set 0 is the seeded host recipe; the other sets (only there to
+    # defeat caching) come from a seeded device generator
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20251203)
+    sets = []
+    for k in range(args.decode_sets):
+        layer = []
+        for p in wl.projs:
+            if k == 0:
+                Wd = torch.from_numpy(synth.normal_f32((p.o, p.d), wl.w_std,
+                                                       [wl.wid, synth.PROJ_IDS[p.name], synth.T_W])).to(dev)
+            else:
+                Wd = torch.empty((p.o, p.d), dtype=torch.float32, device=dev)
+                Wd.normal_(0.0, wl.w_std, generator=gen)
+            layer.append((p, qb.qlora_quantize_nf4_dq(Wd, check_finite=False)))
+            del Wd
+        sets.append(layer)
+    def bfd(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    adapters = {p.name: (bfd(synth.normal_bf16((p.d, wl.r), 0.02, [wl.wid, synth.PROJ_IDS[p.name], synth.T_A])),
+                         bfd(synth.normal_bf16((wl.r, p.o), 0.02, [wl.wid, synth.PROJ_IDS[p.name], synth.T_B])))
+                for p in wl.projs}
+    res = {}
+    ws = qb.Workspace()
+    for M in (1, 4, 16):
+        xs = {p.name: torch.from_numpy(synth.normal_bf16((M, p.d), 1.0, [wl.wid, synth.PROJ_IDS[p.name],
+                                                                         synth.T_X]).view(np.int16))
+              .view(torch.bfloat16).to(dev) for p in wl.projs}
+        ys = {p.name: torch.empty((M, p.o), dtype=torch.bfloat16, device=dev) for p in wl.projs}
+        byts = 0
+        for p in wl.projs:
+            c, s8, s2 = qb.qlora_quant_sizes(p.o * p.d)
+            byts += c + s8 + s2 + 2 * (p.d * wl.r + wl.r * p.o + M * p.d + M * p.o)
+
+        def one(layer):
+            for p, qw in layer:
+                A, B = adapters[p.name]
+                qb.qlora_linear_fwd(xs[p.name], qw, A, B, wl.s, want_T=False, ws=ws, out=ys[p.name])
+
+        for layer in sets[:4]:
+            one(layer)
+        torch.cuda.synchronize()
+        reps = max(2, 96 // len(sets))
+        qb.qlora_timing_begin()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            for layer in sets:
+                one(layer)
+        e1.record()
+        torch.cuda.synchronize()
+        qb.qlora_timing_end()
+        n = reps * len(sets)
+        us = e0.elapsed_time(e1) * 1e3 / n
+        gemv_ms, gemv_n = qb.qlora_timing_read(qb.K_GEMV)
+        res[f"M{M}"] = {"us_per_mlp": round(us, 2), "bytes_per_mlp": byts,
+                        "GBps": round(byts / (us * 1e-6) / 1e9, 1),
+                        "frac_of_hbm": round(byts / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+                        "gemv_kernel_us": round(gemv_ms * 1e3 / max(gemv_n, 1), 2) if gemv_n else None}
+    return {"workload": "decode_mlp_7b: gate/up 4096->11008, down 11008->4096, r=16, fwd only",
+            "weight_sets_cycled": len(sets), "peak_GBps": PEAK_HBM_GBPS, **res}
+
+
+def cpu_baseline(args, wl, p):
+    """The oracle as it stands (fp64 NumPy), on the host, on the same workload."""
+    import numpy as np
+
+    import synth
+    from oracle import linear, nf4
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max(i.get("num_threads", 1) for i in threadpool_info())
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    W, X, A, B, dY = synth.layer_inputs(wl, p)
+    f = nf4.bf16_bits_to_f64
+    Xf, Af, Bf, dYf = f(X), f(A), f(B), f(dY)
+    times = []
+    t_start = time.perf_counter()
+    while time.perf_counter() - t_start < args.cpu_seconds or len(times) < 2:
+        t = time.perf_counter()
+        c, s8, s2 = nf4.quantize_chunked(W.ravel())
+        Wh = f(nf4.dequant_bf16_bits(c, s8, s2, W.size)).reshape(W.shape)
+        linear.forward(Xf, Wh, Af, Bf, wl.s)
+        linear.backward(dYf, Xf, Wh, Af, Bf, wl.s)
+        times.append(time.perf_counter() - t)
+        if len(times) >= 20:
+            break
+    med = statistics.median(times)
+    M, d, o, r = wl.M, p.d, p.o, wl.r
+    return {"value": round(step_flops(M, d, o, r) / med / 1e12, 5), "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle", "s_per_step": round(med, 3), "steps_timed": len(times),
+            "sample": f"full {wl.name} step (quantize+dequant+fwd+bwd, fp64 NumPy/OpenBLAS), "
+                      f"median of {len(times)}"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,203 @@
+/*
+ * qlora.h -- C ABI of the NF4 + double-quantization QLoRA linear layer,
+ *            hand-written HIP kernels for AMD Instinct MI355X (gfx950).
+ *
+ * Source of the method (cited by page title and section):
+ *   [QLoRA-074] "074｜QLoRA：把大模型放进显存，再用小适配器改变它"
+ *               (wq-win.github.io/llm/074-qlora.html), a summary of Dettmers
+ *               et al., "QLoRA: Efficient Finetuning of Quantized LLMs", 2023.
+ *
+ * The layer (QLoRA-074 §一, problem setting):
+ *     Y = X·Ŵ + s·X·A·B,   Ŵ = Dequant(W4bit, scales),
+ *     X ∈ R^{M×d}, Ŵ ∈ R^{d×o}, A ∈ R^{d×r}, B ∈ R^{r×o}.
+ * The 4-bit weight is frozen: training updates A and B only, but the input
+ * gradient still multiplies by Ŵᵀ (QLoRA-074, note on what the backward pass
+ * still needs).  There is deliberately no weight gradient in this ABI.
+ *
+ * Storage conventions shared by every entry point
+ *   - The weight is stored as nn.Linear stores it, Wq[o][d] row-major, so
+ *     Ŵ = Wqᵀ.  Quantization sees it as a flat array of n = o·d fp32 values,
+ *     element i = row·d + col.
+ *   - Block b = i / 64 has one first-level constant (absmax), group
+ *     g = b / 256 one fp32 second-level constant (QLoRA-074 §二).  For the
+ *     linear entry points d must be a multiple of 64, so blocks run along d.
+ *   - codes: ceil(n/2) bytes; element 2j in bits 3:0 of byte j, element 2j+1
+ *     in bits 7:4; a missing last element is padded with code 7 (zero).
+ *   - scale8: ceil(n/64) bytes, unsigned linear code q of the block absmax:
+ *     ĉ_b = fl32(q_b · step_g).
+ *   - scale2: ceil(n/16384) fp32 values, step_g = fl32(max c1 in g / 255).
+ *   - Dequantized weight ŵ_i = fl32(V[k_i] · ĉ_b) with V the 16-value NF4
+ *     codebook (qlora_codebook); the linear layer uses RNE_bf16(ŵ_i).
+ *   - bf16 tensors are raw bfloat16 bit patterns (uint16_t), row-major,
+ *     contiguous.
+ *
+ * Memory and execution
+ *   - Every tensor pointer is caller-allocated DEVICE memory, 16-byte aligned,
+ *     unless stated otherwise.  The library never allocates or frees device
+ *     memory; scratch comes from the caller's workspace (qlora_workspace_bytes).
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL means
+ *     the null stream).  Nothing synchronizes the host.
+ *   - Calls that share a workspace must be ordered (same stream); calls with
+ *     separate workspaces are independent.  No kernel uses atomics, so every
+ *     result is bitwise reproducible run to run.
+ *
+ * Errors: every entry point returns a qlora_status.  Argument checks happen
+ * before anything is launched; on error nothing was enqueued.
+ */
+#ifndef QLORA_H_
+#define QLORA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QLORA_BLOCK 64      /* weights per first-level (absmax) block        */
+#define QLORA_GROUP 256     /* first-level constants per second-level step   */
+#define QLORA_MAX_RANK 256  /* largest LoRA rank r accepted                  */
+
+typedef enum {
+  QLORA_OK = 0,
+  QLORA_E_INVALID = 1,    /* null pointer where one is required, bad enum, n < 0 */
+  QLORA_E_SHAPE = 2,      /* d % 64 != 0, r out of range or not a multiple of 8,
+                             negative sizes, n != o*d                          */
+  QLORA_E_ALIGN = 3,      /* a tensor pointer is not 16-byte aligned          */
+  QLORA_E_WORKSPACE = 4,  /* ws_bytes below qlora_workspace_bytes()          */
+  QLORA_E_NO_DEVICE = 5,  /* no HIP device visible to the process            */
+  QLORA_E_HIP = 6,        /* a HIP launch or runtime call failed             */
+  QLORA_E_NONFINITE = 7   /* reserved for bindings: a flag word had bit 0 set */
+} qlora_status;
+
+typedef enum { QLORA_F32 = 0, QLORA_BF16 = 1 } qlora_dtype;
+
+typedef enum {
+  QLORA_OP_FWD = 0,       /* workspace of qlora_linear_fwd */
+  QLORA_OP_BWD = 1        /* workspace of qlora_linear_bwd */
+} qlora_op;
+
+typedef uint16_t qlora_bf16; /* raw bfloat16 bits */
+
+/* Non-owning view of a quantized tensor (QLoRA-074 §三: the frozen W4 codes
+ * plus the 8-bit first-level and fp32 second-level constants).  All three
+ * buffers are device memory sized by qlora_quant_sizes(n). */
+typedef struct qlora_nf4dq {
+  uint8_t* codes;   /* ceil(n/2) bytes        */
+  uint8_t* scale8;  /* ceil(n/64) bytes       */
+  float* scale2;    /* ceil(n/16384) floats   */
+  int64_t n;        /* number of weights      */
+} qlora_nf4dq;
+
+/* ---------------------------------------------------------------- host helpers */
+
+/* Byte sizes of the three buffers of n weights (QLoRA-074, boxed note on the
+ * compression ratio: 16384 weights -> 8192 code bytes + 256 + 4 bytes of
+ * constants).  Any output pointer may be NULL.  Pure host code. */
+int qlora_quant_sizes(int64_t n, int64_t* codes_bytes, int64_t* scale8_bytes,
+                      int64_t* scale2_bytes);
+
+/* The 16 NF4 values as fp32, ascending, generated on the host at load time
+ * from normal quantiles (QLoRA-074 §二): 8 positive values
+ * Φ⁻¹(1/2 + j(p−1/2)/8), 7 negative −Φ⁻¹(1/2 + j(p−1/2)/7), and 0, all over
+ * Φ⁻¹(p), p = 1 − (1/32 + 1/30)/2.  `out` is host memory for 16 floats. */
+int qlora_codebook(float* out);
+
+/* Workspace in bytes needed by qlora_linear_fwd (op = QLORA_OP_FWD) or
+ * qlora_linear_bwd (op = QLORA_OP_BWD) for these sizes.  Returns 0 for
+ * invalid sizes.  Pure host code. */
+size_t qlora_workspace_bytes(int op, int64_t M, int64_t d, int64_t o, int64_t r);
+
+const char* qlora_strerror(int status);
+const char* qlora_version(void);
+
+/* ------------------------------------------------------------ device entry points */
+
+/* Blockwise NF4 quantization with double quantization of the constants
+ * (QLoRA-074 §三 procedure: blockwise NF4 quantize with block 64, then
+ * quantize the first-level constants with block 256; §二 NF4 and double
+ * quantization).
+ *   W      device fp32[n], any values; n >= 0 (n = 0 is a no-op).
+ *   out    view of caller buffers sized by qlora_quant_sizes(n); out->n must
+ *          equal n.  Overwritten entirely.
+ *   d_flags device int32 or NULL.  If any weight is NaN or ±Inf, bit 0 is set
+ *          (the word is never cleared by the library; zero it first).  The
+ *          outputs of a group holding a non-finite weight are unspecified.
+ * Per block: c1 = max |w|; each weight gets the index of the codebook value
+ * nearest to w/c1 (exact comparison, ties to the lower index); a zero block
+ * gets code 7.  Per group: step = fl32(max c1 / 255); q = the integer in
+ * 0..255 nearest to c1/step (ties to the lower), 0 if step is 0. */
+int qlora_quantize_nf4_dq(const float* W, int64_t n, const qlora_nf4dq* out,
+                          int32_t* d_flags, void* stream);
+
+/* Dequantization Ŵ = Dequant(W4bit, scales) (QLoRA-074 §一; §三 "dequantize
+ * the required weights to BF16").
+ *   q          quantized tensor (device buffers), q->n >= 0.
+ *   out_dtype  QLORA_F32: out is fp32[n] with ŵ_i = fl32(V[k]·fl32(q8·step));
+ *              QLORA_BF16: out is bf16[n] holding RNE_bf16(ŵ_i).
+ * Bit-exact by construction: two IEEE fp32 products, nearest-even rounding. */
+int qlora_dequant(const qlora_nf4dq* q, int out_dtype, void* out, void* stream);
+
+/* Forward of the QLoRA linear layer (QLoRA-074 §一):
+ *     T = X·A,   Y = X·Ŵ + s·T·B,   Ŵ = Wqᵀ.
+ *   X      bf16[M][d]       A  bf16[d][r]      B  bf16[r][o]
+ *   W      quantized Wq[o][d], W->n == o*d, d % 64 == 0
+ *   s      adapter scale (α/r in LoRA); r == 0 or s == 0 runs the base only
+ *   Y      bf16[M][o] (output, overwritten)
+ *   T_out  fp32[M][r] or NULL: if given, receives T = X·A (for the backward)
+ *   ws     device workspace of at least qlora_workspace_bytes(QLORA_OP_FWD,...)
+ * Products use bf16 operands (the dequantized weight rounded to bf16) with
+ * fp32 accumulation; Y is rounded to bf16 once.  M == 0 is a no-op.
+ * 0 <= r <= 256 and r % 8 == 0; A and B may be NULL only if r == 0. */
+int qlora_linear_fwd(const qlora_bf16* X, int64_t M, int64_t d,
+                     const qlora_nf4dq* W, int64_t o,
+                     const qlora_bf16* A, const qlora_bf16* B, int64_t r, float s,
+                     qlora_bf16* Y, float* T_out,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* Backward of the QLoRA linear layer (QLoRA-074 §一 and the note on what the
+ * backward pass still needs): with U = dY·Bᵀ,
+ *     dX = dY·Ŵᵀ + s·U·Aᵀ,   dA = s·Xᵀ·U,   dB = s·Tᵀ·dY,   T = X·A.
+ * No gradient is produced for the frozen 4-bit weight.
+ *   dY     bf16[M][o]        X bf16[M][d] (both may be NULL when M == 0)
+ *   T      fp32[M][r] from qlora_linear_fwd's T_out, or NULL to recompute it
+ *   W, A, B, s, r as in qlora_linear_fwd
+ *   dX     bf16[M][d] or NULL (skip the input gradient)
+ *   dA     bf16[d][r], dB bf16[r][o]: overwritten (not accumulated); may be
+ *          NULL only if r == 0
+ *   ws     device workspace of at least qlora_workspace_bytes(QLORA_OP_BWD,...)
+ * M == 0 writes zeros to dA and dB. */
+int qlora_linear_bwd(const qlora_bf16* dY, const qlora_bf16* X, const float* T,
+                     int64_t M, int64_t d, const qlora_nf4dq* W, int64_t o,
+                     const qlora_bf16* A, const qlora_bf16* B, int64_t r, float s,
+                     qlora_bf16* dX, qlora_bf16* dA, qlora_bf16* dB,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------ diagnostics */
+
+/* Kernel classes timed by the diagnostics below. */
+typedef enum {
+  QLORA_K_MAIN_GEMM = 0,  /* fused X·Ŵ (+adapter) and dY·Ŵᵀ (+adapter) products */
+  QLORA_K_QUANTIZE = 1,   /* blockwise NF4 + double-quant kernel                  */
+  QLORA_K_GEMV = 2,       /* few-token dequant-GEMV forward                       */
+  QLORA_K_DEQUANT = 3,    /* standalone / transposed dequant kernels              */
+  QLORA_K_ADAPTER = 4,    /* rank-r products T = X·A, U = dY·Bᵀ and their sums    */
+  QLORA_K_GRADS = 5,      /* dA, dB products over the tokens and their sums       */
+  QLORA_K_COUNT = 6
+} qlora_kernel_class;
+
+/* Launch timing for benchmarks: between qlora_timing_begin() and
+ * qlora_timing_end(), every launch of the library records a pair of HIP
+ * events on its own stream around the kernel(s) of its class.
+ * qlora_timing_read() waits for those events and returns the summed elapsed
+ * milliseconds and the number of launches of one class.  Process-wide, not
+ * thread-safe; meant for single-threaded benchmark drivers. */
+int qlora_timing_begin(void);
+int qlora_timing_end(void);
+int qlora_timing_read(int kernel_class, double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLORA_H_ */

@@ -1,0 +1,280 @@
+"""Python binding of libqlora.so, the MI355X (gfx950) QLoRA NF4 + double-quant layer.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI of include/qlora.h.  PyTorch provides device memory
+and the current HIP stream.  There is no CPU fallback: if the library is not
+built, or a tensor is not on a HIP device, the calls raise.
+
+Functions carry the C names:
+  qlora_quant_sizes, qlora_codebook, qlora_workspace_bytes,
+  qlora_quantize_nf4_dq, qlora_dequant, qlora_linear_fwd, qlora_linear_bwd.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libqlora.so")
+
+QLORA_OK, QLORA_E_NONFINITE = 0, 7
+QLORA_F32, QLORA_BF16 = 0, 1
+QLORA_OP_FWD, QLORA_OP_BWD = 0, 1
+
+_lib = None
+
+
+class QloraError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {strerror(status)} (status {status})")
+
+
+class _NF4DQ(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scale8", ctypes.c_void_p),
+                ("scale2", ctypes.c_void_p), ("n", ctypes.c_int64)]
+
+
+def lib() -> ctypes.CDLL:
+    """Load libqlora.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -c "
+                           f"'import __graft_entry__ as g; g.build()'` (no CPU fallback exists)")
+    L = ctypes.CDLL(LIB_PATH)
+    i64, vp, sz, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    P = ctypes.POINTER
+    L.qlora_quant_sizes.argtypes = [i64, P(i64), P(i64), P(i64)]
+    L.qlora_codebook.argtypes = [P(ctypes.c_float)]
+    L.qlora_workspace_bytes.argtypes = [i32, i64, i64, i64, i64]
+    L.qlora_workspace_bytes.restype = sz
+    L.qlora_strerror.argtypes = [i32]
+    L.qlora_strerror.restype = ctypes.c_char_p
+    L.qlora_version.restype = ctypes.c_char_p
+    L.qlora_quantize_nf4_dq.argtypes = [vp, i64, P(_NF4DQ), vp, vp]
+    L.qlora_dequant.argtypes = [P(_NF4DQ), i32, vp, vp]
+    L.qlora_linear_fwd.argtypes = [vp, i64, i64, P(_NF4DQ), i64, vp, vp, i64, ctypes.c_float,
+                                   vp, vp, vp, sz, vp]
+    L.qlora_linear_bwd.argtypes = [vp, vp, vp, i64, i64, P(_NF4DQ), i64, vp, vp, i64,
+                                   ctypes.c_float, vp, vp, vp, vp, sz, vp]
+    L.qlora_timing_read.argtypes = [i32, P(ctypes.c_double), P(i64)]
+    for name in ("qlora_quant_sizes", "qlora_codebook", "qlora_quantize_nf4_dq", "qlora_dequant",
+                 "qlora_linear_fwd", "qlora_linear_bwd", "qlora_timing_begin", "qlora_timing_end",
+                 "qlora_timing_read"):
+        getattr(L, name).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def strerror(status: int) -> str:
+    return lib().qlora_strerror(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != QLORA_OK:
+        raise QloraError(status, where)
+
+
+# ------------------------------------------------------------------ host helpers
+
+def qlora_quant_sizes(n: int) -> tuple[int, int, int]:
+    c, s8, s2 = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().qlora_quant_sizes(n, ctypes.byref(c), ctypes.byref(s8), ctypes.byref(s2)),
+           "qlora_quant_sizes")
+    return c.value, s8.value, s2.value
+
+
+def qlora_codebook() -> list[float]:
+    buf = (ctypes.c_float * 16)()
+    _check(lib().qlora_codebook(buf), "qlora_codebook")
+    return list(buf)
+
+
+def qlora_workspace_bytes(op: int, M: int, d: int, o: int, r: int) -> int:
+    return int(lib().qlora_workspace_bytes(op, M, d, o, r))
+
+
+# Kernel classes of the launch-timing diagnostics (qlora_kernel_class).
+K_MAIN_GEMM, K_QUANTIZE, K_GEMV, K_DEQUANT, K_ADAPTER, K_GRADS = range(6)
+KERNEL_CLASSES = {"main_gemm": K_MAIN_GEMM, "quantize": K_QUANTIZE, "gemv": K_GEMV,
+                  "dequant": K_DEQUANT, "adapter": K_ADAPTER, "grads": K_GRADS}
+
+
+def qlora_timing_begin():
+    _check(lib().qlora_timing_begin(), "qlora_timing_begin")
+
+
+def qlora_timing_end():
+    _check(lib().qlora_timing_end(), "qlora_timing_end")
+
+
+def qlora_timing_read(kernel_class: int) -> tuple[float, int]:
+    """(summed milliseconds, launches) of one kernel class since qlora_timing_begin()."""
+    ms, n = ctypes.c_double(), ctypes.c_int64()
+    _check(lib().qlora_timing_read(kernel_class, ctypes.byref(ms), ctypes.byref(n)),
+           "qlora_timing_read")
+    return ms.value, n.value
+
+
+# ------------------------------------------------------------------ device calls
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, dtype, name, device=None):
+    torch = _torch()
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise TypeError(f"{name} must be a HIP device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+@dataclass
+class QuantizedWeight:
+    """Device buffers of a quantized tensor: codes, 8-bit scales, fp32 steps."""
+    codes: object
+    scale8: object
+    scale2: object
+    n: int
+    shape: tuple
+
+    def view(self) -> _NF4DQ:
+        return _NF4DQ(self.codes.data_ptr(), self.scale8.data_ptr(), self.scale2.data_ptr(), self.n)
+
+    @property
+    def device(self):
+        return self.codes.device
+
+
+def _alloc_quantized(n: int, shape, device) -> QuantizedWeight:
+    torch = _torch()
+    c, s8, s2 = qlora_quant_sizes(n)
+    return QuantizedWeight(torch.empty(max(c, 1), dtype=torch.uint8, device=device),
+                           torch.empty(max(s8, 1), dtype=torch.uint8, device=device),
+                           torch.empty(max(s2 // 4, 1), dtype=torch.float32, device=device),
+                           n, tuple(shape))
+
+
+def qlora_quantize_nf4_dq(W, check_finite: bool = True, out: QuantizedWeight | None = None
+                          ) -> QuantizedWeight:
+    """Blockwise NF4 + double quantization of an fp32 device tensor (any shape, flattened).
+
+    `out` reuses the buffers of an earlier result of the same size.  With
+    check_finite the call waits for the kernel and raises on NaN/Inf input.
+    """
+    torch = _torch()
+    _need(W, torch.float32, "W")
+    if out is not None and out.n != W.numel():
+        raise ValueError("out holds a different number of weights")
+    q = _alloc_quantized(W.numel(), W.shape, W.device) if out is None else out
+    flags = getattr(q, "flags", None)
+    if flags is None:
+        flags = torch.zeros(1, dtype=torch.int32, device=W.device)
+    elif check_finite:
+        flags.zero_()
+    _check(lib().qlora_quantize_nf4_dq(_ptr(W), W.numel(), ctypes.byref(q.view()), _ptr(flags),
+                                       _stream(W.device)), "qlora_quantize_nf4_dq")
+    if check_finite and int(flags.item()) & 1:
+        raise QloraError(QLORA_E_NONFINITE, "qlora_quantize_nf4_dq")
+    q.flags = flags
+    return q
+
+
+def qlora_dequant(q: QuantizedWeight, dtype=None):
+    """Ŵ as fp32 (default) or bf16, shaped like the original tensor."""
+    torch = _torch()
+    dtype = torch.float32 if dtype is None else dtype
+    code = {torch.float32: QLORA_F32, torch.bfloat16: QLORA_BF16}[dtype]
+    out = torch.empty(q.shape, dtype=dtype, device=q.device)
+    _check(lib().qlora_dequant(ctypes.byref(q.view()), code, _ptr(out), _stream(q.device)),
+           "qlora_dequant")
+    return out
+
+
+class Workspace:
+    """Grow-only device scratch buffer reused across calls on one stream."""
+
+    def __init__(self, device=None):
+        self.device = device
+        self.buf = None
+
+    def get(self, nbytes: int, device):
+        torch = _torch()
+        if self.buf is None or self.buf.numel() < nbytes or self.buf.device != device:
+            self.buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        return self.buf
+
+
+_default_ws: dict = {}
+
+
+def _workspace(ws, device, nbytes):
+    if ws is None:
+        ws = _default_ws.setdefault(str(device), Workspace())
+    return ws.get(nbytes, device)
+
+
+def qlora_linear_fwd(X, q: QuantizedWeight, A, B, s: float, want_T: bool = True, ws=None,
+                     out=None):
+    """Y = X·Ŵ + s·(X·A)·B.  X bf16 [M][d]; q of Wq [o][d]; A bf16 [d][r]; B bf16 [r][o].
+
+    Returns (Y, T) with T = X·A in fp32 (None if want_T is False or r == 0).
+    """
+    torch = _torch()
+    M, d = X.shape
+    o = q.shape[0]
+    r = 0 if A is None else A.shape[1]
+    for t, nm in ((X, "X"), (A, "A"), (B, "B")):
+        _need(t, torch.bfloat16, nm, X.device)
+    Y = torch.empty((M, o), dtype=torch.bfloat16, device=X.device) if out is None else out
+    _need(Y, torch.bfloat16, "Y", X.device)
+    T = torch.empty((M, r), dtype=torch.float32, device=X.device) if (want_T and r > 0) else None
+    nbytes = qlora_workspace_bytes(QLORA_OP_FWD, M, d, o, r)
+    buf = _workspace(ws, X.device, nbytes)
+    _check(lib().qlora_linear_fwd(_ptr(X), M, d, ctypes.byref(q.view()), o, _ptr(A), _ptr(B), r,
+                                  float(s), _ptr(Y), _ptr(T), _ptr(buf), buf.numel(),
+                                  _stream(X.device)), "qlora_linear_fwd")
+    return Y, T
+
+
+def qlora_linear_bwd(dY, X, T, q: QuantizedWeight, A, B, s: float, need_dX: bool = True,
+                     ws=None):
+    """(dX, dA, dB) of the layer; no gradient for the 4-bit weight.  T may be None."""
+    torch = _torch()
+    M, o = dY.shape
+    d = q.shape[1]
+    r = 0 if A is None else A.shape[1]
+    for t, nm in ((dY, "dY"), (X, "X"), (A, "A"), (B, "B")):
+        _need(t, torch.bfloat16, nm, dY.device)
+    _need(T, torch.float32, "T", dY.device)
+    dev = dY.device
+    dX = torch.empty((M, d), dtype=torch.bfloat16, device=dev) if need_dX else None
+    dA = torch.empty((d, r), dtype=torch.bfloat16, device=dev) if r > 0 else None
+    dB = torch.empty((r, o), dtype=torch.bfloat16, device=dev) if r > 0 else None
+    nbytes = qlora_workspace_bytes(QLORA_OP_BWD, M, d, o, r)
+    buf = _workspace(ws, dev, nbytes)
+    _check(lib().qlora_linear_bwd(_ptr(dY), _ptr(X), _ptr(T), M, d, ctypes.byref(q.view()), o,
+                                  _ptr(A), _ptr(B), r, float(s), _ptr(dX), _ptr(dA), _ptr(dB),
+                                  _ptr(buf), buf.numel(), _stream(dev)), "qlora_linear_bwd")
+    return dX, dA, dB

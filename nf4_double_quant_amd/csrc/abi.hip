@@ -1,0 +1,384 @@
+// extern "C" entry points declared in include/qlora.h: argument checks,
+// workspace layout and the launch sequence of each operation.
+#include <string.h>
+
+#include <utility>
+#include <vector>
+
+#include "kernels.h"
+#include "qlora.h"
+
+
+using namespace qlora;
+
+namespace {
+
+constexpr int64_t kAlign = 256;
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t up(int64_t a) { return cdiv(a, kAlign) * kAlign; }
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+inline int64_t clampi(int64_t v, int64_t lo, int64_t hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+// Split counts: enough workgroups to cover the 256 CUs about twice.
+int64_t splits_nt(int64_t M, int64_t N, int64_t K) {
+  const int64_t tiles = cdiv(M, 64) * cdiv(N, 64);
+  if (tiles == 0) return 1;
+  return clampi(cdiv(512, tiles), 1, clampi(cdiv(K, 64), 1, 16));
+}
+int64_t splits_tn(int64_t P, int64_t Q, int64_t Mtok) {
+  const int64_t tiles = P <= 64 ? cdiv(P, 64) * cdiv(Q, 128) : cdiv(P, 128) * cdiv(Q, 64);
+  if (tiles == 0) return 1;
+  return clampi(cdiv(512, tiles), 1, clampi(cdiv(Mtok, 64), 1, 32));
+}
+
+struct FwdLayout {
+  bool gemv;                                   // few-token path
+  int64_t At, Bt, Tpart, sT, What, Xp, total;  // byte offsets into the workspace
+  int64_t sT_splits;
+};
+FwdLayout fwd_layout(int64_t M, int64_t d, int64_t o, int64_t r) {
+  FwdLayout L{};
+  int64_t off = 0;
+  L.gemv = M <= kGemvMaxTokens;
+  if (L.gemv) {
+    L.sT_splits = gemv_tsplits(d);
+    L.Xp = off;    off += up(2 * M * d);
+    L.Tpart = off; off += up(4 * L.sT_splits * M * r);
+  } else {
+    L.sT_splits = r > 0 ? splits_nt(M, r, d) : 0;
+    L.At = off;    off += up(2 * r * d);
+    L.Bt = off;    off += up(2 * o * r);
+    L.Tpart = off; off += up(4 * L.sT_splits * M * r);
+    L.sT = off;    off += up(2 * M * r);
+    L.What = off;  off += up(2 * o * d);
+  }
+  L.total = off;
+  return L;
+}
+
+struct BwdLayout {
+  int64_t At, Tpart, sT, Upart, sU, dApart, dBpart, WT, total;
+  int64_t t_splits, u_splits, a_splits, b_splits;
+};
+BwdLayout bwd_layout(int64_t M, int64_t d, int64_t o, int64_t r) {
+  BwdLayout L{};
+  int64_t off = 0;
+  if (r > 0) {
+    L.t_splits = splits_nt(M, r, d);
+    L.u_splits = splits_nt(M, r, o);
+    L.a_splits = splits_tn(d, r, M);
+    L.b_splits = splits_tn(r, o, M);
+  }
+  L.At = off;     off += up(2 * r * d);
+  L.Tpart = off;  off += up(4 * L.t_splits * M * r);
+  L.sT = off;     off += up(2 * M * r);
+  L.Upart = off;  off += up(4 * L.u_splits * M * r);
+  L.sU = off;     off += up(2 * M * r);
+  L.dApart = off; off += up(4 * L.a_splits * d * r);
+  L.dBpart = off; off += up(4 * L.b_splits * r * o);
+  L.WT = off;     off += up(2 * d * o);
+  L.total = off;
+  return L;
+}
+
+int device_status() {
+  static int cached = -1;
+  if (cached < 0) {
+    int n = 0;
+    cached = (hipGetDeviceCount(&n) == hipSuccess && n > 0) ? QLORA_OK : QLORA_E_NO_DEVICE;
+  }
+  return cached;
+}
+
+// Event pairs recorded around launches while timing is on (diagnostics only).
+struct LaunchTimer {
+  bool on = false;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> ev[QLORA_K_COUNT];
+  void clear() {
+    for (auto& v : ev) {
+      for (auto& p : v) {
+        hipEventDestroy(p.first);
+        hipEventDestroy(p.second);
+      }
+      v.clear();
+    }
+  }
+};
+LaunchTimer g_timer;
+
+template <class F>
+hipError_t timed(int cls, hipStream_t st, F&& f) {
+  if (!g_timer.on) return f();
+  hipEvent_t a, b;
+  if (hipEventCreate(&a) != hipSuccess) return hipErrorUnknown;
+  if (hipEventCreate(&b) != hipSuccess) {
+    hipEventDestroy(a);
+    return hipErrorUnknown;
+  }
+  hipEventRecord(a, st);
+  const hipError_t e = f();
+  hipEventRecord(b, st);
+  g_timer.ev[cls].push_back({a, b});
+  return e;
+}
+
+#define QL_TRY(expr)                                  \
+  do {                                                \
+    if ((expr) != hipSuccess) return QLORA_E_HIP;     \
+  } while (0)
+
+// Launch one kernel of class `cls` (timed while diagnostics are on).
+#define QL_RUN(cls, st, expr) QL_TRY(timed((cls), (st), [&]() { return (expr); }))
+
+int check_quant_view(const qlora_nf4dq* q) {
+  if (q == nullptr) return QLORA_E_INVALID;
+  if (q->n < 0) return QLORA_E_INVALID;
+  if (q->n > 0 && (q->codes == nullptr || q->scale8 == nullptr || q->scale2 == nullptr))
+    return QLORA_E_INVALID;
+  if (!aligned16(q->codes) || !aligned16(q->scale8) || !aligned16(q->scale2)) return QLORA_E_ALIGN;
+  return QLORA_OK;
+}
+
+int check_linear_shapes(int64_t M, int64_t d, int64_t o, int64_t r, const qlora_nf4dq* W) {
+  if (M < 0 || d <= 0 || o <= 0 || r < 0) return QLORA_E_SHAPE;
+  if (d % QLORA_BLOCK != 0 || o % 8 != 0) return QLORA_E_SHAPE;
+  if (r > QLORA_MAX_RANK || r % 8 != 0) return QLORA_E_SHAPE;
+  int st = check_quant_view(W);
+  if (st) return st;
+  if (W->n != o * d) return QLORA_E_SHAPE;
+  return QLORA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qlora_quant_sizes(int64_t n, int64_t* codes_bytes, int64_t* scale8_bytes, int64_t* scale2_bytes) {
+  if (n < 0) return QLORA_E_INVALID;
+  const int64_t nb = cdiv(n, QLORA_BLOCK);
+  if (codes_bytes) *codes_bytes = cdiv(n, 2);
+  if (scale8_bytes) *scale8_bytes = nb;
+  if (scale2_bytes) *scale2_bytes = 4 * cdiv(nb, QLORA_GROUP);
+  return QLORA_OK;
+}
+
+int qlora_codebook(float* out) {
+  if (out == nullptr) return QLORA_E_INVALID;
+  memcpy(out, host_codebook().v, sizeof(float) * 16);
+  return QLORA_OK;
+}
+
+size_t qlora_workspace_bytes(int op, int64_t M, int64_t d, int64_t o, int64_t r) {
+  if (M < 0 || d < 0 || o < 0 || r < 0 || r > QLORA_MAX_RANK) return 0;
+  if (op == QLORA_OP_FWD) return (size_t)fwd_layout(M, d, o, r).total;
+  if (op == QLORA_OP_BWD) return (size_t)bwd_layout(M, d, o, r).total;
+  return 0;
+}
+
+const char* qlora_strerror(int status) {
+  switch (status) {
+    case QLORA_OK: return "ok";
+    case QLORA_E_INVALID: return "invalid argument";
+    case QLORA_E_SHAPE: return "unsupported shape (need d % 64 == 0, o % 8 == 0, 0 <= r <= 256, r % 8 == 0, n == o*d)";
+    case QLORA_E_ALIGN: return "tensor pointer not 16-byte aligned";
+    case QLORA_E_WORKSPACE: return "workspace too small";
+    case QLORA_E_NO_DEVICE: return "no HIP device available";
+    case QLORA_E_HIP: return "HIP runtime or launch failure";
+    case QLORA_E_NONFINITE: return "non-finite weight in quantizer input";
+    default: return "unknown status";
+  }
+}
+
+const char* qlora_version(void) { return "qlora-mi355x 0.1.0 (gfx950)"; }
+
+int qlora_timing_begin(void) {
+  g_timer.clear();
+  g_timer.on = true;
+  return QLORA_OK;
+}
+
+int qlora_timing_end(void) {
+  g_timer.on = false;
+  return QLORA_OK;
+}
+
+int qlora_timing_read(int kernel_class, double* total_ms, int64_t* launches) {
+  if (kernel_class < 0 || kernel_class >= QLORA_K_COUNT) return QLORA_E_INVALID;
+  double sum = 0.0;
+  for (auto& p : g_timer.ev[kernel_class]) {
+    if (hipEventSynchronize(p.second) != hipSuccess) return QLORA_E_HIP;
+    float ms = 0.0f;
+    if (hipEventElapsedTime(&ms, p.first, p.second) != hipSuccess) return QLORA_E_HIP;
+    sum += ms;
+  }
+  if (total_ms) *total_ms = sum;
+  if (launches) *launches = (int64_t)g_timer.ev[kernel_class].size();
+  return QLORA_OK;
+}
+
+int qlora_quantize_nf4_dq(const float* W, int64_t n, const qlora_nf4dq* out, int32_t* d_flags,
+                          void* stream) {
+  if (n < 0 || out == nullptr) return QLORA_E_INVALID;
+  if (n > 0 && W == nullptr) return QLORA_E_INVALID;
+  int st = check_quant_view(out);
+  if (st) return st;
+  if (out->n != n) return QLORA_E_SHAPE;
+  if (!aligned16(W)) return QLORA_E_ALIGN;
+  if (n == 0) return QLORA_OK;
+  if ((st = device_status())) return st;
+  QL_RUN(QLORA_K_QUANTIZE, (hipStream_t)stream, launch_quantize(W, n, out->codes, out->scale8, out->scale2, d_flags, (hipStream_t)stream));
+  return QLORA_OK;
+}
+
+int qlora_dequant(const qlora_nf4dq* q, int out_dtype, void* out, void* stream) {
+  int st = check_quant_view(q);
+  if (st) return st;
+  if (out_dtype != QLORA_F32 && out_dtype != QLORA_BF16) return QLORA_E_INVALID;
+  if (q->n > 0 && out == nullptr) return QLORA_E_INVALID;
+  if (!aligned16(out)) return QLORA_E_ALIGN;
+  if (q->n == 0) return QLORA_OK;
+  if ((st = device_status())) return st;
+  QL_RUN(QLORA_K_DEQUANT, (hipStream_t)stream, launch_dequant(q->codes, q->scale8, q->scale2, q->n, out_dtype == QLORA_BF16, out,
+                        (hipStream_t)stream));
+  return QLORA_OK;
+}
+
+int qlora_linear_fwd(const qlora_bf16* X, int64_t M, int64_t d, const qlora_nf4dq* W, int64_t o,
+                     const qlora_bf16* A, const qlora_bf16* B, int64_t r, float s, qlora_bf16* Y,
+                     float* T_out, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_linear_shapes(M, d, o, r, W);
+  if (st) return st;
+  if (M > 0 && (X == nullptr || Y == nullptr)) return QLORA_E_INVALID;
+  if (r > 0 && (A == nullptr || B == nullptr)) return QLORA_E_INVALID;
+  if (!aligned16(X) || !aligned16(Y) || !aligned16(A) || !aligned16(B) || !aligned16(T_out) ||
+      !aligned16(ws))
+    return QLORA_E_ALIGN;
+  const FwdLayout L = fwd_layout(M, d, o, r);
+  if (ws_bytes < (size_t)L.total) return QLORA_E_WORKSPACE;
+  if (L.total > 0 && ws == nullptr) return QLORA_E_WORKSPACE;
+  if (M == 0) return QLORA_OK;
+  if ((st = device_status())) return st;
+  hipStream_t hs = (hipStream_t)stream;
+  char* w = static_cast<char*>(ws);
+  uint16_t* At = reinterpret_cast<uint16_t*>(w + L.At);
+  uint16_t* Bt = reinterpret_cast<uint16_t*>(w + L.Bt);
+  float* Tpart = reinterpret_cast<float*>(w + L.Tpart);
+  uint16_t* sT = reinterpret_cast<uint16_t*>(w + L.sT);
+  uint16_t* What = reinterpret_cast<uint16_t*>(w + L.What);
+  const bool lora = r > 0 && s != 0.0f;
+
+  if (L.gemv) {
+    QL_RUN(QLORA_K_GEMV, hs,
+           launch_gemv_fwd(X, (int)M, d, W->codes, W->scale8, W->scale2, o, A, B, (int)r, s, Y,
+                           T_out, reinterpret_cast<uint16_t*>(w + L.Xp), Tpart, hs));
+    return QLORA_OK;
+  }
+  if (r > 0 && (lora || T_out != nullptr)) {
+    // T = X·A as X·(Aᵀ)ᵀ with split-K over d
+    QL_RUN(QLORA_K_ADAPTER, hs, launch_transpose_bf16(A, d, r, At, hs));
+    GemmArgs g{};
+    g.A = X; g.lda = d; g.B = At; g.ldb = d;
+    g.M = M; g.N = r; g.K = d; g.C = Tpart; g.ldc = r;
+    QL_RUN(QLORA_K_ADAPTER, hs, launch_gemm_nt_splitk(g, (int)L.sT_splits, hs));
+    QL_RUN(QLORA_K_ADAPTER, hs, launch_reduce_planes(Tpart, (int)L.sT_splits, M * r, M, r, r, T_out, r,
+                                lora ? sT : nullptr, r, s, hs));
+  }
+  if (lora) QL_RUN(QLORA_K_ADAPTER, hs, launch_transpose_bf16(B, r, o, Bt, hs));
+  QL_RUN(QLORA_K_DEQUANT, hs, launch_dequant(W->codes, W->scale8, W->scale2, W->n, true, What, hs));
+  GemmArgs g{};
+  g.A = X; g.lda = d; g.B = What; g.ldb = d;
+  g.A2 = sT; g.lda2 = r; g.B2 = Bt; g.ldb2 = r;
+  g.M = M; g.N = o; g.K = d; g.K2 = lora ? r : 0;
+  g.C = Y; g.ldc = o;
+  QL_RUN(QLORA_K_MAIN_GEMM, hs, launch_gemm_nt_bf16(g, hs));
+  return QLORA_OK;
+}
+
+int qlora_linear_bwd(const qlora_bf16* dY, const qlora_bf16* X, const float* T, int64_t M, int64_t d,
+                     const qlora_nf4dq* W, int64_t o, const qlora_bf16* A, const qlora_bf16* B,
+                     int64_t r, float s, qlora_bf16* dX, qlora_bf16* dA, qlora_bf16* dB, void* ws,
+                     size_t ws_bytes, void* stream) {
+  int st = check_linear_shapes(M, d, o, r, W);
+  if (st) return st;
+  if (M > 0 && dY == nullptr) return QLORA_E_INVALID;
+  if (r > 0 && (A == nullptr || B == nullptr || dA == nullptr || dB == nullptr ||
+                (M > 0 && X == nullptr)))
+    return QLORA_E_INVALID;
+  if (dX == nullptr && r == 0) return QLORA_OK;
+  if (!aligned16(dY) || !aligned16(X) || !aligned16(T) || !aligned16(A) || !aligned16(B) ||
+      !aligned16(dX) || !aligned16(dA) || !aligned16(dB) || !aligned16(ws))
+    return QLORA_E_ALIGN;
+  const BwdLayout L = bwd_layout(M, d, o, r);
+  if (ws_bytes < (size_t)L.total) return QLORA_E_WORKSPACE;
+  if (L.total > 0 && ws == nullptr) return QLORA_E_WORKSPACE;
+  if ((st = device_status())) return st;
+  hipStream_t hs = (hipStream_t)stream;
+  if (M == 0) {
+    if (r > 0) {
+      QL_RUN(QLORA_K_GRADS, hs, launch_fill_zero_bf16(dA, d * r, hs));
+      QL_RUN(QLORA_K_GRADS, hs, launch_fill_zero_bf16(dB, r * o, hs));
+    }
+    return QLORA_OK;
+  }
+  char* w = static_cast<char*>(ws);
+  uint16_t* At = reinterpret_cast<uint16_t*>(w + L.At);
+  float* Tpart = reinterpret_cast<float*>(w + L.Tpart);
+  uint16_t* sT = reinterpret_cast<uint16_t*>(w + L.sT);
+  float* Upart = reinterpret_cast<float*>(w + L.Upart);
+  uint16_t* sU = reinterpret_cast<uint16_t*>(w + L.sU);
+  float* dApart = reinterpret_cast<float*>(w + L.dApart);
+  float* dBpart = reinterpret_cast<float*>(w + L.dBpart);
+  uint16_t* WT = reinterpret_cast<uint16_t*>(w + L.WT);
+
+  if (r > 0) {
+    // s·T in bf16 (operand of dB = (sT)ᵀ·dY)
+    if (T != nullptr) {
+      QL_RUN(QLORA_K_ADAPTER, hs, launch_scale_to_bf16(T, M * r, s, sT, hs));
+    } else {
+      QL_RUN(QLORA_K_ADAPTER, hs, launch_transpose_bf16(A, d, r, At, hs));
+      GemmArgs g{};
+      g.A = X; g.lda = d; g.B = At; g.ldb = d;
+      g.M = M; g.N = r; g.K = d; g.C = Tpart; g.ldc = r;
+      QL_RUN(QLORA_K_ADAPTER, hs, launch_gemm_nt_splitk(g, (int)L.t_splits, hs));
+      QL_RUN(QLORA_K_ADAPTER, hs, launch_reduce_planes(Tpart, (int)L.t_splits, M * r, M, r, r, nullptr, r, sT, r, s, hs));
+    }
+    // s·U = s·dY·Bᵀ; B[r][o] is already the K-major operand
+    {
+      GemmArgs g{};
+      g.A = dY; g.lda = o; g.B = B; g.ldb = o;
+      g.M = M; g.N = r; g.K = o; g.C = Upart; g.ldc = r;
+      QL_RUN(QLORA_K_ADAPTER, hs, launch_gemm_nt_splitk(g, (int)L.u_splits, hs));
+      QL_RUN(QLORA_K_ADAPTER, hs, launch_reduce_planes(Upart, (int)L.u_splits, M * r, M, r, r, nullptr, r, sU, r, s, hs));
+    }
+    // dA = Xᵀ·(s·U)   [d][r], reduction over tokens
+    {
+      GemmArgs g{};
+      g.A = X; g.lda = d; g.B = sU; g.ldb = r;
+      g.M = d; g.N = r; g.K = M; g.C = dApart; g.ldc = r;
+      QL_RUN(QLORA_K_GRADS, hs, launch_gemm_tn_splitk(g, (int)L.a_splits, hs));
+      QL_RUN(QLORA_K_GRADS, hs, launch_reduce_planes(dApart, (int)L.a_splits, d * r, d, r, r, nullptr, r, dA, r, 1.0f, hs));
+    }
+    // dB = (s·T)ᵀ·dY  [r][o]
+    {
+      GemmArgs g{};
+      g.A = sT; g.lda = r; g.B = dY; g.ldb = o;
+      g.M = r; g.N = o; g.K = M; g.C = dBpart; g.ldc = o;
+      QL_RUN(QLORA_K_GRADS, hs, launch_gemm_tn_splitk(g, (int)L.b_splits, hs));
+      QL_RUN(QLORA_K_GRADS, hs, launch_reduce_planes(dBpart, (int)L.b_splits, r * o, r, o, o, nullptr, o, dB, o, 1.0f, hs));
+    }
+  }
+  if (dX != nullptr) {
+    const bool lora = r > 0 && s != 0.0f;
+    QL_RUN(QLORA_K_DEQUANT, hs, launch_dequant_t(W->codes, W->scale8, W->scale2, o, d, WT, hs));
+    GemmArgs g{};
+    g.A = dY; g.lda = o; g.B = WT; g.ldb = o;
+    g.A2 = sU; g.lda2 = r; g.B2 = A; g.ldb2 = r;
+    g.M = M; g.N = d; g.K = o; g.K2 = lora ? r : 0;
+    g.C = dX; g.ldc = d;
+    QL_RUN(QLORA_K_MAIN_GEMM, hs, launch_gemm_nt_bf16(g, hs));
+  }
+  return QLORA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,44 @@
+// Shared device types and helpers of the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qlora {
+
+constexpr int kBlock = 64;     // weights per absmax block
+constexpr int kGroup = 256;    // blocks per double-quant group
+constexpr int kGroupElems = kBlock * kGroup;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Codebook handed to kernels by value (kernel arguments live in SGPR-loaded
+// constant memory): the 16 fp32 values and the 15 fp64 midpoints between
+// neighbours, (V[t] + V[t+1]) / 2, which are exact in fp64.
+struct Codebook {
+  float v[16];
+  double mid[15];
+};
+
+// Host-side codebook, built once when the library loads.
+const Codebook& host_codebook();
+
+__device__ __forceinline__ uint16_t bf16_bits(float x) {
+  // gfx950 converts with round-to-nearest-even (v_cvt_pk_bf16_f32).
+  __bf16 h = (__bf16)x;
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)bf16_bits(lo) | ((uint32_t)bf16_bits(hi) << 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+}  // namespace qlora

@@ -1,0 +1,317 @@
+// Blockwise NF4 quantization with double quantization, and dequantization.
+//
+// Method: "074｜QLoRA：把大模型放进显存，再用小适配器改变它" §二 (NF4 codes,
+// absmax per 64 weights, 8-bit first-level constants with one fp32
+// second-level constant per 256 of them) and §三 (quantize the weights with
+// the first-level constants, then quantize those constants).
+//
+// gfx950 design
+//  * One workgroup per double-quant group (16384 weights = 64 KB of fp32):
+//    the group's second-level constant needs every block's absmax, so the
+//    whole group stays in VGPRs (16 float4 per lane) between the reduction
+//    and the encode, and HBM is read exactly once.
+//  * 16 lanes per 64-weight block, one float4 each: every load instruction
+//    covers 1 KB contiguous.  The block absmax is a 16-lane xor-shuffle max
+//    on the integer bits of |w| (integer order equals float order for
+//    non-negative floats, and NaN/Inf land above every finite value, which
+//    is how non-finite input is detected).
+//  * Exact nearest-value encode without fp64 per weight: for each block the
+//    15 decision points c1·mid_t are exact fp64 products; rounding each one
+//    DOWN to fp32 gives a threshold th_t with  w > c1·mid_t  <=>  w > th_t
+//    for every fp32 w.  A thread per block builds them once; each weight
+//    then takes a 4-level branch-free binary search in fp32.
+//  * Codes are gathered in LDS and written out as 16-byte stores.
+#include "kernels.h"
+
+namespace qlora {
+
+// Largest fp32 <= the exact (nonzero) fp64 value p.
+__device__ __forceinline__ float round_down_f32(double p) {
+  float f = (float)p;
+  if ((double)f > p) {
+    int32_t bits = __float_as_int(f);
+    f = __int_as_float(bits > 0 ? bits - 1 : bits + 1);  // toward −inf
+  }
+  return f;
+}
+
+// Number of thresholds strictly below w (= the NF4 code), thresholds ascending.
+__device__ __forceinline__ uint32_t nf4_search(float w, const float (&t)[16]) {
+  const bool b3 = w > t[7];
+  const bool b2 = w > (b3 ? t[11] : t[3]);
+  const float t1 = b3 ? (b2 ? t[13] : t[9]) : (b2 ? t[5] : t[1]);
+  const bool b1 = w > t1;
+  const float t0 = b3 ? (b2 ? (b1 ? t[14] : t[12]) : (b1 ? t[10] : t[8]))
+                      : (b2 ? (b1 ? t[6] : t[4]) : (b1 ? t[2] : t[0]));
+  const bool b0 = w > t0;
+  return ((uint32_t)b3 << 3) | ((uint32_t)b2 << 2) | ((uint32_t)b1 << 1) | (uint32_t)b0;
+}
+
+__device__ __forceinline__ uint32_t abs_bits(float x) { return __float_as_uint(x) & 0x7FFFFFFFu; }
+
+__global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, int64_t n,
+                                                  uint8_t* __restrict__ codes,
+                                                  uint8_t* __restrict__ scale8,
+                                                  float* __restrict__ scale2,
+                                                  int32_t* __restrict__ flags, Codebook cb) {
+  __shared__ __attribute__((aligned(16))) float s_thr[kGroup][16];
+  __shared__ __attribute__((aligned(16))) uint16_t s_codes[kGroupElems / 4];
+  __shared__ uint32_t s_c1[kGroup];
+  __shared__ uint32_t s_red[4];
+
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int sub = lane & 15, quad = lane >> 4;
+  const int64_t g = blockIdx.x;
+  const int64_t base = g * kGroupElems;
+  const int64_t nb = (n + kBlock - 1) / kBlock;
+
+  // ---- load the group (zeros past n) and take per-block absmax
+  float4 v[16];
+  uint32_t bad = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int bl = wave * 64 + j * 4 + quad;
+    const int64_t e = base + (int64_t)bl * kBlock + sub * 4;
+    if (e + 4 <= n) {
+      v[j] = *reinterpret_cast<const float4*>(W + e);
+    } else {
+      v[j].x = e + 0 < n ? W[e + 0] : 0.0f;
+      v[j].y = e + 1 < n ? W[e + 1] : 0.0f;
+      v[j].z = e + 2 < n ? W[e + 2] : 0.0f;
+      v[j].w = e + 3 < n ? W[e + 3] : 0.0f;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    uint32_t a = max(max(abs_bits(v[j].x), abs_bits(v[j].y)), max(abs_bits(v[j].z), abs_bits(v[j].w)));
+    a = max(a, (uint32_t)__shfl_xor((int)a, 8, 16));
+    a = max(a, (uint32_t)__shfl_xor((int)a, 4, 16));
+    a = max(a, (uint32_t)__shfl_xor((int)a, 2, 16));
+    a = max(a, (uint32_t)__shfl_xor((int)a, 1, 16));
+    bad |= (a >= 0x7F800000u);
+    if (sub == 0) s_c1[wave * 64 + j * 4 + quad] = a;
+  }
+  __syncthreads();
+
+  // ---- second level: one thread per block
+  const uint32_t c1_bits = s_c1[t];
+  uint32_t m = c1_bits;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
+  if (lane == 0) s_red[wave] = m;
+  __syncthreads();
+  m = max(max(s_red[0], s_red[1]), max(s_red[2], s_red[3]));
+  const float c1 = __uint_as_float(c1_bits);
+  const float c2 = __uint_as_float(m);
+  // fp64 quotient of fp32 operands rounded to fp32 is the correctly rounded quotient.
+  const float step = (float)((double)c2 / 255.0);
+
+  uint32_t q = 0;
+  if (step > 0.0f) {
+    const double cd = (double)c1, sd = (double)step;
+    double qf = floor(cd / sd);
+    if (!(qf < 255.0)) qf = 255.0;
+    const int q0 = (int)qf;
+    // Exact: (2q0+1)·step has at most 33 significant bits.
+    q = (uint32_t)q0 + (cd > (2.0 * (double)q0 + 1.0) * sd * 0.5 ? 1u : 0u);
+    q = min(q, 255u);
+  }
+  const int64_t b_glob = g * kGroup + t;
+  if (b_glob < nb) scale8[b_glob] = (uint8_t)q;
+  if (t == 0) scale2[g] = step;
+
+  // decision thresholds of this block
+  {
+    float th[16];
+    if (c1_bits == 0) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) th[i] = i < 7 ? -1.0f : 0.0f;  // everything -> code 7
+    } else {
+#pragma unroll
+      for (int i = 0; i < 15; ++i) th[i] = round_down_f32((double)c1 * cb.mid[i]);
+      th[15] = 0.0f;
+    }
+    float4* dst = reinterpret_cast<float4*>(&s_thr[t][0]);
+    dst[0] = make_float4(th[0], th[1], th[2], th[3]);
+    dst[1] = make_float4(th[4], th[5], th[6], th[7]);
+    dst[2] = make_float4(th[8], th[9], th[10], th[11]);
+    dst[3] = make_float4(th[12], th[13], th[14], th[15]);
+  }
+  __syncthreads();
+
+  // ---- encode
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int bl = wave * 64 + j * 4 + quad;
+    const float4* src = reinterpret_cast<const float4*>(&s_thr[bl][0]);
+    float th[16];
+    const float4 t0 = src[0], t1 = src[1], t2 = src[2], t3 = src[3];
+    th[0] = t0.x; th[1] = t0.y; th[2] = t0.z; th[3] = t0.w;
+    th[4] = t1.x; th[5] = t1.y; th[6] = t1.z; th[7] = t1.w;
+    th[8] = t2.x; th[9] = t2.y; th[10] = t2.z; th[11] = t2.w;
+    th[12] = t3.x; th[13] = t3.y; th[14] = t3.z; th[15] = t3.w;
+    const uint32_t k0 = nf4_search(v[j].x, th);
+    const uint32_t k1 = nf4_search(v[j].y, th);
+    const uint32_t k2 = nf4_search(v[j].z, th);
+    const uint32_t k3 = nf4_search(v[j].w, th);
+    s_codes[bl * 16 + sub] = (uint16_t)(k0 | (k1 << 4) | (k2 << 8) | (k3 << 12));
+  }
+  __syncthreads();
+
+  // ---- write the group's 8192 code bytes
+  const int64_t code_bytes = (n + 1) / 2;
+  const int64_t cbase = g * (kGroupElems / 2);
+  const int64_t off = cbase + (int64_t)t * 32;
+  const uint8_t* sc = reinterpret_cast<const uint8_t*>(s_codes) + t * 32;
+  if (off + 32 <= code_bytes) {
+    uint4* dst = reinterpret_cast<uint4*>(codes + off);
+    dst[0] = reinterpret_cast<const uint4*>(sc)[0];
+    dst[1] = reinterpret_cast<const uint4*>(sc)[1];
+  } else {
+    for (int i = 0; i < 32; ++i)
+      if (off + i < code_bytes) codes[off + i] = sc[i];
+  }
+  if (bad && flags != nullptr) flags[0] = flags[0] | 1;
+}
+
+// ------------------------------------------------------------------ dequant
+// Eight weights per thread (one code dword); ŵ = fl32(V[k]·fl32(q8·step)).
+template <bool kBf16>
+__global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ codes,
+                                                 const uint8_t* __restrict__ scale8,
+                                                 const float* __restrict__ scale2, int64_t n,
+                                                 void* __restrict__ out, Codebook cb) {
+  __shared__ float s_v[16];
+  if (threadIdx.x < 16) s_v[threadIdx.x] = cb.v[threadIdx.x];
+  __syncthreads();
+  const int64_t n8 = (n + 7) / 8;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t e0 = i * 8;
+    const int64_t b = e0 / kBlock;
+    const float chat = (float)scale8[b] * scale2[b / kGroup];
+    uint32_t w;
+    if (e0 + 8 <= n) {
+      w = reinterpret_cast<const uint32_t*>(codes)[i];
+    } else {
+      w = 0;
+      const int64_t cb_bytes = (n + 1) / 2;
+      for (int k = 0; k < 4; ++k)
+        if (i * 4 + k < cb_bytes) w |= (uint32_t)codes[i * 4 + k] << (8 * k);
+    }
+    float r[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) r[k] = s_v[(w >> (4 * k)) & 15u] * chat;
+    if (kBf16) {
+      uint16_t* o = reinterpret_cast<uint16_t*>(out);
+      if (e0 + 8 <= n && ((reinterpret_cast<uintptr_t>(o + e0) & 15) == 0)) {
+        uint4 pk;
+        pk.x = pack_bf16x2(r[0], r[1]);
+        pk.y = pack_bf16x2(r[2], r[3]);
+        pk.z = pack_bf16x2(r[4], r[5]);
+        pk.w = pack_bf16x2(r[6], r[7]);
+        *reinterpret_cast<uint4*>(o + e0) = pk;
+      } else {
+        for (int k = 0; k < 8; ++k)
+          if (e0 + k < n) o[e0 + k] = bf16_bits(r[k]);
+      }
+    } else {
+      float* o = reinterpret_cast<float*>(out);
+      if (e0 + 8 <= n) {
+        reinterpret_cast<float4*>(o + e0)[0] = make_float4(r[0], r[1], r[2], r[3]);
+        reinterpret_cast<float4*>(o + e0)[1] = make_float4(r[4], r[5], r[6], r[7]);
+      } else {
+        for (int k = 0; k < 8; ++k)
+          if (e0 + k < n) o[e0 + k] = r[k];
+      }
+    }
+  }
+}
+
+// Transposed bf16 dequant of a row-major Wq[o][d] (d % 64 == 0) into WT[d][o],
+// the K-major operand of the input-gradient product.  One 64×64 tile (64 rows,
+// one block each) per workgroup, transposed through LDS.
+__global__ __launch_bounds__(256) void k_dequant_t(const uint8_t* __restrict__ codes,
+                                                   const uint8_t* __restrict__ scale8,
+                                                   const float* __restrict__ scale2, int64_t o,
+                                                   int64_t d, uint16_t* __restrict__ WT,
+                                                   Codebook cb) {
+  __shared__ uint16_t tile[64][66];
+  __shared__ float s_v[16];
+  if (threadIdx.x < 16) s_v[threadIdx.x] = cb.v[threadIdx.x];
+  __syncthreads();
+  const int t = threadIdx.x;
+  const int64_t o0 = (int64_t)blockIdx.y * 64, d0 = (int64_t)blockIdx.x * 64;
+  {
+    const int row = t >> 2, q = t & 3;
+    const int64_t orow = o0 + row;
+    if (orow < o) {
+      const int64_t e0 = orow * d + d0 + q * 16;
+      const int64_t b = e0 / kBlock;
+      const float chat = (float)scale8[b] * scale2[b / kGroup];
+      const uint2 w2 = *reinterpret_cast<const uint2*>(codes + e0 / 2);
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const uint32_t w = k < 8 ? w2.x : w2.y;
+        tile[row][q * 16 + k] = bf16_bits(s_v[(w >> (4 * (k & 7))) & 15u] * chat);
+      }
+    }
+  }
+  __syncthreads();
+  {
+    const int col = t >> 2, q = t & 3;   // output row d0+col, o range o0+16q..
+    const int64_t drow = d0 + col;
+    uint16_t vals[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) vals[k] = tile[q * 16 + k][col];
+    uint16_t* dst = WT + drow * o + o0 + q * 16;
+    if (o0 + q * 16 + 16 <= o && (o % 8) == 0) {
+      uint4 a, b;
+      a.x = vals[0] | ((uint32_t)vals[1] << 16);   a.y = vals[2] | ((uint32_t)vals[3] << 16);
+      a.z = vals[4] | ((uint32_t)vals[5] << 16);   a.w = vals[6] | ((uint32_t)vals[7] << 16);
+      b.x = vals[8] | ((uint32_t)vals[9] << 16);   b.y = vals[10] | ((uint32_t)vals[11] << 16);
+      b.z = vals[12] | ((uint32_t)vals[13] << 16); b.w = vals[14] | ((uint32_t)vals[15] << 16);
+      reinterpret_cast<uint4*>(dst)[0] = a;
+      reinterpret_cast<uint4*>(dst)[1] = b;
+    } else {
+      for (int k = 0; k < 16; ++k)
+        if (o0 + q * 16 + k < o) dst[k] = vals[k];
+    }
+  }
+}
+
+// ------------------------------------------------------------------ launchers
+hipError_t launch_quantize(const float* W, int64_t n, uint8_t* codes, uint8_t* scale8,
+                           float* scale2, int32_t* flags, hipStream_t st) {
+  const int64_t ng = (n + kGroupElems - 1) / kGroupElems;
+  if (ng == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_quantize, dim3((unsigned)ng), dim3(256), 0, st, W, n, codes, scale8,
+                     scale2, flags, host_codebook());
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scale8, const float* scale2,
+                          int64_t n, bool bf16, void* out, hipStream_t st) {
+  const int64_t n8 = (n + 7) / 8;
+  if (n8 == 0) return hipSuccess;
+  int64_t blocks = (n8 + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  if (bf16)
+    hipLaunchKernelGGL(k_dequant<true>, dim3((unsigned)blocks), dim3(256), 0, st, codes, scale8,
+                       scale2, n, out, host_codebook());
+  else
+    hipLaunchKernelGGL(k_dequant<false>, dim3((unsigned)blocks), dim3(256), 0, st, codes, scale8,
+                       scale2, n, out, host_codebook());
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant_t(const uint8_t* codes, const uint8_t* scale8, const float* scale2,
+                            int64_t o, int64_t d, uint16_t* WT, hipStream_t st) {
+  if (o == 0 || d == 0) return hipSuccess;
+  dim3 grid((unsigned)(d / 64), (unsigned)((o + 63) / 64));
+  hipLaunchKernelGGL(k_dequant_t, grid, dim3(256), 0, st, codes, scale8, scale2, o, d, WT,
+                     host_codebook());
+  return hipGetLastError();
+}
+
+}  // namespace qlora

@@ -1,0 +1,126 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel is launched).
+
+* the library loads and exports every function include/qlora.h declares;
+* size helpers match the oracle and the pages' worked example;
+* the library's host-generated codebook equals the oracle's bit for bit
+  (two independent constructions: C++ Newton on erfc vs Python AS241);
+* argument validation returns its status before anything touches a device;
+* without a visible device, valid calls return QLORA_E_NO_DEVICE.
+"""
+
+import ctypes
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import nf4
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qlora.h")
+
+qb = pytest.importorskip("nf4_double_quant_amd")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(qb.LIB_PATH):
+        pytest.fail("libqlora.so is not built (run __graft_entry__.build())")
+    return qb.lib()
+
+
+def declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qlora_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert len(names) >= 9
+    for name in names:
+        assert hasattr(L, name), name
+
+
+def test_quant_sizes_match_oracle_and_worked_example(L):
+    with open(os.path.join(ROOT, "tests", "golden", "worked_example.json"), encoding="utf-8") as f:
+        g = json.load(f)
+    assert qb.qlora_quant_sizes(g["weights"]) == (g["code_bytes"], g["scale8_bytes"], g["scale2_bytes"])
+    for n in (0, 1, 63, 64, 65, 16383, 16384, 16385, 4096 * 11008, 22016 * 8192):
+        assert qb.qlora_quant_sizes(n) == nf4.sizes(n)
+    assert L.qlora_quant_sizes(-1, None, None, None) == 1
+
+
+def test_library_codebook_equals_oracle(L):
+    lib_v = np.array(qb.qlora_codebook(), dtype=np.float32)
+    assert lib_v.tobytes() == nf4.codebook().tobytes()
+
+
+def test_workspace_and_strings(L):
+    assert qb.qlora_workspace_bytes(qb.QLORA_OP_FWD, 4096, 4096, 4096, 64) > 2 * 4096 * 4096
+    assert qb.qlora_workspace_bytes(qb.QLORA_OP_BWD, 4096, 4096, 4096, 64) > 0
+    assert qb.qlora_workspace_bytes(7, 1, 64, 8, 8) == 0
+    for op in (qb.QLORA_OP_FWD, qb.QLORA_OP_BWD):       # empty sizes are valid queries
+        for M, d, o, r in ((0, 128, 64, 8), (8, 0, 64, 8), (8, 128, 0, 8), (0, 0, 0, 0), (1, 64, 8, 0)):
+            qb.qlora_workspace_bytes(op, M, d, o, r)
+    assert qb.qlora_workspace_bytes(qb.QLORA_OP_FWD, 1, 64, 8, 512) == 0
+    assert "gfx950" in L.qlora_version().decode()
+    for st in range(8):
+        assert qb.strerror(st)
+
+
+# Fake, never-dereferenced device addresses: validation must fail (or, for a
+# valid call, the device probe must) before any pointer is used.
+A16 = 0x10000
+
+
+def _view(n, codes=A16, s8=A16, s2=A16):
+    return qb._NF4DQ(codes, s8, s2, n)
+
+
+def test_validation_statuses(L):
+    fwd = L.qlora_linear_fwd
+    v = _view(128 * 128)
+    args = dict(X=A16, M=8, d=128, o=128, A=A16, B=A16, r=8, s=2.0, Y=A16, T=None, ws=A16,
+                wsb=1 << 30)
+
+    def call(**kw):
+        a = {**args, **kw}
+        return fwd(a["X"], a["M"], a["d"], ctypes.byref(kw.get("view", v)), a["o"], a["A"], a["B"],
+                   a["r"], a["s"], a["Y"], a["T"], a["ws"], a["wsb"], None)
+
+    assert call(d=100, view=_view(128 * 100)) == 2          # d % 64
+    assert call(o=100, view=_view(100 * 128)) == 2          # o % 8
+    assert call(r=12) == 2                                  # r % 8
+    assert call(r=264) == 2                                 # r > 256
+    assert call(view=_view(128 * 127)) == 2                 # n != o*d
+    assert call(X=A16 + 2) == 3                             # alignment
+    assert call(view=_view(128 * 128, codes=A16 + 4)) == 3
+    assert call(wsb=16) == 4                                # workspace
+    assert call(A=None) == 1                                # adapters required for r > 0
+    assert call(M=-1) == 2
+    # quantize / dequant
+    q = L.qlora_quantize_nf4_dq
+    assert q(A16, -5, ctypes.byref(_view(0)), None, None) == 1
+    assert q(A16, 100, ctypes.byref(_view(99)), None, None) == 2
+    assert q(A16 + 8, 100, ctypes.byref(_view(100)), None, None) == 3
+    assert L.qlora_dequant(ctypes.byref(_view(100)), 5, A16, None) == 1
+    # bwd
+    bwd = L.qlora_linear_bwd
+    assert bwd(A16, A16, None, 8, 128, ctypes.byref(v), 128, A16, A16, 8, 2.0, A16, None, A16,
+               A16, 1 << 30, None) == 1                     # dA missing
+
+
+def test_no_device_status(L):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    v = _view(128 * 128)
+    assert L.qlora_quantize_nf4_dq(A16, 128 * 128, ctypes.byref(v), None, None) == 5
+    assert L.qlora_dequant(ctypes.byref(v), 0, A16, None) == 5
+    assert L.qlora_linear_fwd(A16, 8, 128, ctypes.byref(v), 128, A16, A16, 8, 2.0, A16, None,
+                              A16, 1 << 30, None) == 5
+    # size-0 work is a no-op even without a device
+    assert L.qlora_quantize_nf4_dq(A16, 0, ctypes.byref(_view(0)), None, None) == 0
