@@ -6,9 +6,11 @@ fp64 or exact arithmetic; written from the pages, not from any library.
 Layout (reading of the pages): the tensor is a flat array of n fp32 weights.
 Element i lies in block b = i // 64 and double-quant group g = b // 256.
 For a linear layer stored row-major as Wq[o][d], i = row*d + col, so blocks
-run along d.  Codes are packed two per byte, element 2j in bits 3:0 of byte j
-and element 2j+1 in bits 7:4; a missing last element is padded with code 7
-(the zero code).
+run along d.  The pages fix 4 bits per code (two per byte) but not their
+order; the reading taken packs each run of 8 consecutive codes into one
+little-endian 32-bit word, byte j (j = 0..3) holding code j in bits 3:0 and
+code j+4 in bits 7:4.  Missing codes past n are padded with code 7 (the zero
+code), so the code buffer is 4·ceil(n/8) bytes (n/2 whenever 8 divides n).
 """
 
 from __future__ import annotations
@@ -91,7 +93,7 @@ def sizes(n: int) -> tuple[int, int, int]:
     """Bytes of (codes, 8-bit scales, fp32 second-level scales) for n weights."""
     nb = -(-n // BLOCK)
     ng = -(-nb // GROUP)
-    return -(-n // 2), nb, 4 * ng
+    return 4 * (-(-n // 8)), nb, 4 * ng
 
 
 # --------------------------------------------------------------------------
@@ -134,19 +136,19 @@ def nf4_encode(w: np.ndarray, c1: np.ndarray, V: np.ndarray) -> np.ndarray:
 
 
 def pack_nibbles(k: np.ndarray) -> np.ndarray:
-    """Two 4-bit codes per byte: element 2j low nibble, 2j+1 high nibble."""
+    """4-bit codes -> bytes: per 8 codes one 32-bit word, byte j = k_j | k_{j+4} << 4."""
     k = np.asarray(k, dtype=np.uint8).ravel()
-    if k.size % 2:
-        k = np.concatenate([k, np.array([7], dtype=np.uint8)])
-    return (k[0::2] | (k[1::2] << 4)).astype(np.uint8)
+    pad = (-k.size) % 8
+    if pad:
+        k = np.concatenate([k, np.full(pad, 7, dtype=np.uint8)])
+    g = k.reshape(-1, 8)
+    return (g[:, :4] | (g[:, 4:] << 4)).astype(np.uint8).ravel()
 
 
 def unpack_nibbles(codes: np.ndarray, n: int) -> np.ndarray:
-    codes = np.asarray(codes, dtype=np.uint8)
-    k = np.empty(codes.size * 2, dtype=np.uint8)
-    k[0::2] = codes & 0x0F
-    k[1::2] = codes >> 4
-    return k[:n]
+    b = np.asarray(codes, dtype=np.uint8).reshape(-1, 4)
+    k = np.concatenate([b & 0x0F, b >> 4], axis=1)
+    return k.ravel()[:n]
 
 
 def second_level_step(c1: np.ndarray) -> np.ndarray:

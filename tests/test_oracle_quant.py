@@ -276,8 +276,7 @@ def test_tails_and_padding():
         c, q8, st = nf4.quantize(w)
         cb, s8b, s2b = nf4.sizes(n)
         assert c.nbytes == cb and q8.nbytes == s8b and st.nbytes == s2b
-        if n % 2:
-            assert c[-1] >> 4 == 7
+        assert np.all(nf4.unpack_nibbles(c, cb * 2)[n:] == 7)
         wh = nf4.dequant_f32(c, q8, st, n)
         c1 = nf4.block_absmax(w)
         assert np.all(np.abs(wh - w) <= 0.16 * np.repeat(c1, 64)[:n] + 1e-30)
@@ -294,5 +293,10 @@ def test_chunked_equals_whole():
 def test_nibble_order():
     k = np.arange(16, dtype=np.uint8)
     packed = nf4.pack_nibbles(k)
-    assert packed.tolist() == [0x10, 0x32, 0x54, 0x76, 0x98, 0xBA, 0xDC, 0xFE]
+    assert packed.tolist() == [0x40, 0x51, 0x62, 0x73, 0xC8, 0xD9, 0xEA, 0xFB]
     assert nf4.unpack_nibbles(packed, 16).tolist() == k.tolist()
+    # 4 bits per code: two codes per byte whenever 8 divides n; a ragged tail is padded with 7
+    p3 = nf4.pack_nibbles(np.array([1, 2, 3], dtype=np.uint8))
+    assert p3.tolist() == [0x71, 0x72, 0x73, 0x77]
+    for n in (8, 16384, 4096 * 4096):
+        assert nf4.sizes(n)[0] * 2 == n
