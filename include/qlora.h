@@ -21,8 +21,10 @@
  *   - Block b = i / 64 has one first-level constant (absmax), group
  *     g = b / 256 one fp32 second-level constant (QLoRA-074 §二).  For the
  *     linear entry points d must be a multiple of 64, so blocks run along d.
- *   - codes: ceil(n/2) bytes; element 2j in bits 3:0 of byte j, element 2j+1
- *     in bits 7:4; a missing last element is padded with code 7 (zero).
+ *   - codes: 4 bits per weight, 8 consecutive codes per little-endian 32-bit
+ *     word: byte j (0..3) holds code j in bits 3:0 and code j+4 in bits 7:4.
+ *     Codes past n are padded with 7 (the zero code), so the buffer is
+ *     4·ceil(n/8) bytes (n/2 when 8 divides n).
  *   - scale8: ceil(n/64) bytes, unsigned linear code q of the block absmax:
  *     ĉ_b = fl32(q_b · step_g).
  *   - scale2: ceil(n/16384) fp32 values, step_g = fl32(max c1 in g / 255).
@@ -83,7 +85,7 @@ typedef uint16_t qlora_bf16; /* raw bfloat16 bits */
  * plus the 8-bit first-level and fp32 second-level constants).  All three
  * buffers are device memory sized by qlora_quant_sizes(n). */
 typedef struct qlora_nf4dq {
-  uint8_t* codes;   /* ceil(n/2) bytes        */
+  uint8_t* codes;   /* 4*ceil(n/8) bytes      */
   uint8_t* scale8;  /* ceil(n/64) bytes       */
   float* scale2;    /* ceil(n/16384) floats   */
   int64_t n;        /* number of weights      */

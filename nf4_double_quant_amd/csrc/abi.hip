@@ -34,7 +34,7 @@ int64_t splits_tn(int64_t P, int64_t Q, int64_t Mtok) {
 
 struct FwdLayout {
   bool gemv;                                   // few-token path
-  int64_t At, Bt, Tpart, sT, What, Xp, total;  // byte offsets into the workspace
+  int64_t At, Bt, Tpart, sT, total;  // byte offsets into the workspace
   int64_t sT_splits;
 };
 FwdLayout fwd_layout(int64_t M, int64_t d, int64_t o, int64_t r) {
@@ -43,7 +43,6 @@ FwdLayout fwd_layout(int64_t M, int64_t d, int64_t o, int64_t r) {
   L.gemv = M <= kGemvMaxTokens;
   if (L.gemv) {
     L.sT_splits = gemv_tsplits(d);
-    L.Xp = off;    off += up(2 * M * d);
     L.Tpart = off; off += up(4 * L.sT_splits * M * r);
   } else {
     L.sT_splits = r > 0 ? splits_nt(M, r, d) : 0;
@@ -51,14 +50,13 @@ FwdLayout fwd_layout(int64_t M, int64_t d, int64_t o, int64_t r) {
     L.Bt = off;    off += up(2 * o * r);
     L.Tpart = off; off += up(4 * L.sT_splits * M * r);
     L.sT = off;    off += up(2 * M * r);
-    L.What = off;  off += up(2 * o * d);
   }
   L.total = off;
   return L;
 }
 
 struct BwdLayout {
-  int64_t At, Tpart, sT, Upart, sU, dApart, dBpart, WT, total;
+  int64_t At, Tpart, sT, Upart, sU, dApart, dBpart, total;
   int64_t t_splits, u_splits, a_splits, b_splits;
 };
 BwdLayout bwd_layout(int64_t M, int64_t d, int64_t o, int64_t r) {
@@ -77,7 +75,6 @@ BwdLayout bwd_layout(int64_t M, int64_t d, int64_t o, int64_t r) {
   L.sU = off;     off += up(2 * M * r);
   L.dApart = off; off += up(4 * L.a_splits * d * r);
   L.dBpart = off; off += up(4 * L.b_splits * r * o);
-  L.WT = off;     off += up(2 * d * o);
   L.total = off;
   return L;
 }
@@ -157,7 +154,7 @@ extern "C" {
 int qlora_quant_sizes(int64_t n, int64_t* codes_bytes, int64_t* scale8_bytes, int64_t* scale2_bytes) {
   if (n < 0) return QLORA_E_INVALID;
   const int64_t nb = cdiv(n, QLORA_BLOCK);
-  if (codes_bytes) *codes_bytes = cdiv(n, 2);
+  if (codes_bytes) *codes_bytes = 4 * cdiv(n, 8);
   if (scale8_bytes) *scale8_bytes = nb;
   if (scale2_bytes) *scale2_bytes = 4 * cdiv(nb, QLORA_GROUP);
   return QLORA_OK;
@@ -265,13 +262,12 @@ int qlora_linear_fwd(const qlora_bf16* X, int64_t M, int64_t d, const qlora_nf4d
   uint16_t* Bt = reinterpret_cast<uint16_t*>(w + L.Bt);
   float* Tpart = reinterpret_cast<float*>(w + L.Tpart);
   uint16_t* sT = reinterpret_cast<uint16_t*>(w + L.sT);
-  uint16_t* What = reinterpret_cast<uint16_t*>(w + L.What);
   const bool lora = r > 0 && s != 0.0f;
 
   if (L.gemv) {
     QL_RUN(QLORA_K_GEMV, hs,
            launch_gemv_fwd(X, (int)M, d, W->codes, W->scale8, W->scale2, o, A, B, (int)r, s, Y,
-                           T_out, reinterpret_cast<uint16_t*>(w + L.Xp), Tpart, hs));
+                           T_out, Tpart, hs));
     return QLORA_OK;
   }
   if (r > 0 && (lora || T_out != nullptr)) {
@@ -285,13 +281,9 @@ int qlora_linear_fwd(const qlora_bf16* X, int64_t M, int64_t d, const qlora_nf4d
                                 lora ? sT : nullptr, r, s, hs));
   }
   if (lora) QL_RUN(QLORA_K_ADAPTER, hs, launch_transpose_bf16(B, r, o, Bt, hs));
-  QL_RUN(QLORA_K_DEQUANT, hs, launch_dequant(W->codes, W->scale8, W->scale2, W->n, true, What, hs));
-  GemmArgs g{};
-  g.A = X; g.lda = d; g.B = What; g.ldb = d;
-  g.A2 = sT; g.lda2 = r; g.B2 = Bt; g.ldb2 = r;
-  g.M = M; g.N = o; g.K = d; g.K2 = lora ? r : 0;
-  g.C = Y; g.ldc = o;
-  QL_RUN(QLORA_K_MAIN_GEMM, hs, launch_gemm_nt_bf16(g, hs));
+  QL_RUN(QLORA_K_MAIN_GEMM, hs,
+         launch_qgemm(false, X, d, W->codes, W->scale8, W->scale2, d, sT, r, Bt, r, M, o, d,
+                      lora ? r : 0, Y, o, hs));
   return QLORA_OK;
 }
 
@@ -329,7 +321,6 @@ int qlora_linear_bwd(const qlora_bf16* dY, const qlora_bf16* X, const float* T, 
   uint16_t* sU = reinterpret_cast<uint16_t*>(w + L.sU);
   float* dApart = reinterpret_cast<float*>(w + L.dApart);
   float* dBpart = reinterpret_cast<float*>(w + L.dBpart);
-  uint16_t* WT = reinterpret_cast<uint16_t*>(w + L.WT);
 
   if (r > 0) {
     // s·T in bf16 (operand of dB = (sT)ᵀ·dY)
@@ -370,13 +361,10 @@ int qlora_linear_bwd(const qlora_bf16* dY, const qlora_bf16* X, const float* T, 
   }
   if (dX != nullptr) {
     const bool lora = r > 0 && s != 0.0f;
-    QL_RUN(QLORA_K_DEQUANT, hs, launch_dequant_t(W->codes, W->scale8, W->scale2, o, d, WT, hs));
-    GemmArgs g{};
-    g.A = dY; g.lda = o; g.B = WT; g.ldb = o;
-    g.A2 = sU; g.lda2 = r; g.B2 = A; g.ldb2 = r;
-    g.M = M; g.N = d; g.K = o; g.K2 = lora ? r : 0;
-    g.C = dX; g.ldc = d;
-    QL_RUN(QLORA_K_MAIN_GEMM, hs, launch_gemm_nt_bf16(g, hs));
+    if (lora && T != nullptr) QL_RUN(QLORA_K_ADAPTER, hs, launch_transpose_bf16(A, d, r, At, hs));
+    QL_RUN(QLORA_K_MAIN_GEMM, hs,
+           launch_qgemm(true, dY, o, W->codes, W->scale8, W->scale2, d, sU, r, At, d, M, d, o,
+                        lora ? r : 0, dX, d, hs));
   }
   return QLORA_OK;
 }

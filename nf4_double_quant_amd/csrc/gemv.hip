@@ -14,54 +14,89 @@
 //    and expands its 64 codes with byte permutes into bf16 operands of
 //    v_mfma_f32_16x16x32_bf16 — the activations are the 16×32 A operand
 //    (rows m >= M are zero), the dequantized weights the 32×16 B operand;
-//  * the permute expansion yields the 8 weights of a code dword in the order
-//    0,2,4,6,1,3,5,7; the dot product does not care about the order of k as
-//    long as both operands share it, so X is staged once per call in that
-//    order (k_prep_small) instead of permuting per weight;
+//  * codes are stored 8 per word with byte j = code j | code j+4 << 4, so
+//    masking the word with 0x0F0F0F0F and its 4-bit shift yields selector
+//    bytes for codes 0..3 and 4..7 directly, in natural order;
 //  * waves reduce through LDS in a fixed order, then the epilogue adds
 //    s·T·B with T summed from a few split-K planes, and rounds once to bf16.
+//
+// T = X·A for few tokens comes from k_lora_down_small: MFMA 16x16x32 with
+// the activations as the A operand straight from memory and A's columns as
+// the B operand, read from a row-major LDS tile with ds_read_b64_tr_b16
+// (each 16-lane group gathers 4 consecutive k of 16 columns).
 #include "kernels.h"
 
 namespace qlora {
 
-// Reorder each group of 8 activations to 0,2,4,6,1,3,5,7 (bf16 lanes).
-__device__ __forceinline__ uint4 even_odd8(uint4 x) {
-  uint4 y;
-  y.x = __builtin_amdgcn_perm(x.y, x.x, 0x05040100u);  // x0, x2
-  y.y = __builtin_amdgcn_perm(x.w, x.z, 0x05040100u);  // x4, x6
-  y.z = __builtin_amdgcn_perm(x.y, x.x, 0x07060302u);  // x1, x3
-  y.w = __builtin_amdgcn_perm(x.w, x.z, 0x07060302u);  // x5, x7
-  return y;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ s16x4 lds_read_tr(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (s16x4 __attribute__((address_space(3)))*)(p));
 }
 
-// X -> Xp (even/odd order per 8) and split-K planes of T = X·A.
-// Grid: (tsplits); every block also reorders its k-slice of X.
-__global__ __launch_bounds__(256) void k_prep_small(const uint16_t* __restrict__ X, int M, int64_t d,
-                                                    const uint16_t* __restrict__ A, int r,
-                                                    int64_t kslice, uint16_t* __restrict__ Xp,
-                                                    float* __restrict__ Tpart) {
-  const int z = blockIdx.x;
-  const int64_t k0 = (int64_t)z * kslice;
-  const int64_t k1 = min(d, k0 + kslice);
-  // reorder X[m][k0:k1] in 8-element groups
-  const int64_t groups = (k1 - k0) / 8;
-  for (int64_t i = threadIdx.x; i < (int64_t)M * groups; i += blockDim.x) {
-    const int64_t m = i / groups, g = i % groups;
-    const int64_t off = m * d + k0 + g * 8;
-    *reinterpret_cast<uint4*>(Xp + off) = even_odd8(*reinterpret_cast<const uint4*>(X + off));
+// Split-K planes of T = X·A for M <= 16: workgroup (z, c) sums k in
+// [512 z, 512 z + 512) for the adapter columns [64 c, 64 c + 64).
+constexpr int kPrepK = 512;
+constexpr int kPrepStride = 80;  // bf16 per LDS row: 64 + 16 pad, conflict-free transposed reads
+
+__global__ __launch_bounds__(256) void k_lora_down_small(const uint16_t* __restrict__ X, int M,
+                                                         int64_t d, const uint16_t* __restrict__ A,
+                                                         int r, float* __restrict__ Tpart) {
+  __shared__ __attribute__((aligned(16))) uint16_t s_a[kPrepK * kPrepStride];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int64_t k0 = (int64_t)blockIdx.x * kPrepK;
+  const int c0 = blockIdx.y * 64;
+  // stage A[k0:k0+512][c0:c0+64] (zeros outside)
+  for (int i = t; i < kPrepK * 8; i += 256) {
+    const int row = i >> 3, ch = i & 7;
+    const int64_t k = k0 + row;
+    const int col = c0 + ch * 8;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (k < d && col < r) v = *reinterpret_cast<const uint4*>(A + k * r + col);
+    *reinterpret_cast<uint4*>(s_a + row * kPrepStride + ch * 8) = v;
   }
-  // T partial over this k-slice: one (m, j) output per thread per pass
-  for (int i = threadIdx.x; i < M * r; i += blockDim.x) {
-    const int m = i / r, j = i % r;
-    float acc = 0.0f;
-    const uint16_t* xr = X + (int64_t)m * d;
-    for (int64_t k = k0; k < k1; ++k) acc += bf16_to_f32(xr[k]) * bf16_to_f32(A[k * r + j]);
-    Tpart[((int64_t)z * M + m) * r + j] = acc;
+  __syncthreads();
+  f32x4 acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  const int m = lane & 15, g = lane >> 4, s = lane & 15;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int kq = w * 4 + q;                    // 32-wide k step inside the slice
+    const int64_t kx = k0 + kq * 32 + 8 * g;
+    uint4 xv = make_uint4(0, 0, 0, 0);
+    if (m < M && kx < d) xv = *reinterpret_cast<const uint4*>(X + (int64_t)m * d + kx);
+    const bf16x8 a = __builtin_bit_cast(bf16x8, xv);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = kq * 32 + 8 * g + (s >> 2);
+      const int col = j * 16 + 4 * (s & 3);
+      const s16x4 lo = lds_read_tr(s_a + row * kPrepStride + col);
+      const s16x4 hi = lds_read_tr(s_a + (row + 4) * kPrepStride + col);
+      const short __attribute__((ext_vector_type(8))) bv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, bv), acc[j], 0, 0, 0);
+    }
+  }
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(s_a);      // [4 waves][16 m][64 cols]
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) red[(w * 16 + 4 * g + v) * 64 + j * 16 + (lane & 15)] = acc[j][v];
+  __syncthreads();
+  for (int i = t; i < 16 * 64; i += 256) {
+    const int mm = i >> 6, cc = i & 63;
+    if (mm < M && c0 + cc < r) {
+      const float v = red[(0 * 16 + mm) * 64 + cc] + red[(1 * 16 + mm) * 64 + cc] +
+                      red[(2 * 16 + mm) * 64 + cc] + red[(3 * 16 + mm) * 64 + cc];
+      Tpart[((int64_t)blockIdx.x * M + mm) * r + c0 + cc] = v;
+    }
   }
 }
 
 struct GemvArgs {
-  const uint16_t* Xp;   // [M][d], even/odd order per 8
+  const uint16_t* X;    // [M][d]
   const uint8_t* codes; const uint8_t* scale8; const float* scale2;
   const float* Tpart;   // [tsplits][M][r]
   const uint16_t* B;    // [r][o]
@@ -97,20 +132,20 @@ __device__ __forceinline__ uint32_t plane4(const uint32_t (&pl)[4], uint32_t sel
   return (b & mask) | (a & ~mask);
 }
 
-// 8 codes (one dword) -> 8 bf16 in the order 0,2,4,6,1,3,5,7.
+// 8 codes (one word: byte j = code j | code j+4 << 4) -> 8 bf16, natural order.
 __device__ __forceinline__ bf16x8 expand8(const Lut& t, uint32_t w) {
-  const uint32_t se = w & 0x07070707u, so = (w >> 4) & 0x07070707u;
+  const uint32_t s0 = w & 0x07070707u, s1 = (w >> 4) & 0x07070707u;
   // bit 3 of each nibble -> 0xFF per byte, via the byte-sign selectors of v_perm
   const uint32_t w4 = w << 4;
-  const uint32_t me = __builtin_amdgcn_perm(w4 << 8, w4, 0x090B080Au);
-  const uint32_t mo = __builtin_amdgcn_perm(w << 8, w, 0x090B080Au);
-  const uint32_t le = plane4(t.lo, se, me), he = plane4(t.hi, se, me);
-  const uint32_t lo = plane4(t.lo, so, mo), ho = plane4(t.hi, so, mo);
+  const uint32_t m0 = __builtin_amdgcn_perm(w4 << 8, w4, 0x090B080Au);
+  const uint32_t m1 = __builtin_amdgcn_perm(w << 8, w, 0x090B080Au);
+  const uint32_t l0 = plane4(t.lo, s0, m0), h0 = plane4(t.hi, s0, m0);
+  const uint32_t l1 = plane4(t.lo, s1, m1), h1 = plane4(t.hi, s1, m1);
   u32x4 r;
-  r.x = __builtin_amdgcn_perm(he, le, 0x05010400u);
-  r.y = __builtin_amdgcn_perm(he, le, 0x07030602u);
-  r.z = __builtin_amdgcn_perm(ho, lo, 0x05010400u);
-  r.w = __builtin_amdgcn_perm(ho, lo, 0x07030602u);
+  r.x = __builtin_amdgcn_perm(h0, l0, 0x05010400u);  // codes 0, 1
+  r.y = __builtin_amdgcn_perm(h0, l0, 0x07030602u);  // codes 2, 3
+  r.z = __builtin_amdgcn_perm(h1, l1, 0x05010400u);  // codes 4, 5
+  r.w = __builtin_amdgcn_perm(h1, l1, 0x07030602u);  // codes 6, 7
   return __builtin_bit_cast(bf16x8, r);
 }
 
@@ -142,7 +177,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(GemvArgs p) {
     }
     Lut lut;
     build_lut(p.cb, chat, lut);
-    const uint4* xp = reinterpret_cast<const uint4*>(p.Xp + (int64_t)m * p.d + kb * kBlock);
+    const uint4* xp = reinterpret_cast<const uint4*>(p.X + (int64_t)m * p.d + kb * kBlock);
     const bool xok = m_ok && kb < nblk;
     const uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
 #pragma unroll
@@ -184,22 +219,21 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(GemvArgs p) {
   }
 }
 
-int gemv_tsplits(int64_t d) {
-  const int64_t s = d / 512;
-  return (int)(s < 1 ? 1 : (s > 16 ? 16 : s));
-}
+int gemv_tsplits(int64_t d) { return (int)((d + kPrepK - 1) / kPrepK); }
 
 hipError_t launch_gemv_fwd(const uint16_t* X, int M, int64_t d, const uint8_t* codes,
                            const uint8_t* scale8, const float* scale2, int64_t o,
                            const uint16_t* A, const uint16_t* B, int r, float s, uint16_t* Y,
-                           float* T_out, uint16_t* Xp, float* Tpart, hipStream_t st) {
+                           float* T_out, float* Tpart, hipStream_t st) {
   const int ts = gemv_tsplits(d);
-  const int64_t kslice = ((d / 8 + ts - 1) / ts) * 8;
   const int rr = (r > 0 && (s != 0.0f || T_out != nullptr)) ? r : 0;
-  hipLaunchKernelGGL(k_prep_small, dim3(ts), dim3(256), 0, st, X, M, d, A, rr, kslice, Xp, Tpart);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  GemvArgs p{Xp, codes, scale8, scale2, Tpart, B, Y, T_out, d, o, M, rr, ts, s, host_codebook()};
+  if (rr > 0) {
+    hipLaunchKernelGGL(k_lora_down_small, dim3(ts, (rr + 63) / 64), dim3(256), 0, st, X, M, d, A,
+                       rr, Tpart);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  GemvArgs p{X, codes, scale8, scale2, Tpart, B, Y, T_out, d, o, M, rr, ts, s, host_codebook()};
   const unsigned grid = (unsigned)((o + 15) / 16);
   if (o >= 16 * 512)
     hipLaunchKernelGGL(k_gemv<4>, dim3(grid), dim3(256), 0, st, p);

@@ -25,6 +25,15 @@ hipError_t launch_dequant_t(const uint8_t* codes, const uint8_t* scale8, const f
                             int64_t o, int64_t d, uint16_t* WT, hipStream_t st);
 
 hipError_t launch_gemm_nt_bf16(const GemmArgs& a, hipStream_t st);
+
+// Fused NF4 dequant-GEMM: C = A·Ŵ (+ A2·B2) with Ŵ from the quantized Wq[o][d].
+// trans_w = false: forward, C[M][N=o] = A[M][K=d]·Wqᵀ, B2 = Bᵀ [N][K2].
+// trans_w = true:  backward, C[M][N=d] = A[M][K=o]·Wq, B2 = Aᵀ [K2][N].
+hipError_t launch_qgemm(bool trans_w, const uint16_t* A, int64_t lda, const uint8_t* codes,
+                        const uint8_t* scale8, const float* scale2, int64_t d,
+                        const uint16_t* A2, int64_t lda2, const uint16_t* B2, int64_t ldb2,
+                        int64_t M, int64_t N, int64_t K, int64_t K2, uint16_t* C, int64_t ldc,
+                        hipStream_t st);
 hipError_t launch_gemm_nt_splitk(const GemmArgs& a, int splits, hipStream_t st);
 hipError_t launch_gemm_tn_splitk(const GemmArgs& a, int splits, hipStream_t st);
 hipError_t launch_reduce_planes(const float* part, int splits, int64_t plane, int64_t rows,
@@ -36,14 +45,14 @@ hipError_t launch_scale_to_bf16(const float* x, int64_t n, float scale, uint16_t
                                 hipStream_t st);
 hipError_t launch_fill_zero_bf16(uint16_t* y, int64_t n, hipStream_t st);
 
-// Few-token forward (M <= kGemvMaxTokens): Xp [M][d] bf16 and Tpart
-// [gemv_tsplits(d)][M][r] fp32 are workspace.
+// Few-token forward (M <= kGemvMaxTokens): Tpart [gemv_tsplits(d)][M][r]
+// fp32 is workspace.
 constexpr int kGemvMaxTokens = 16;
 constexpr int kMaxGemvRank = 256;
 int gemv_tsplits(int64_t d);
 hipError_t launch_gemv_fwd(const uint16_t* X, int M, int64_t d, const uint8_t* codes,
                            const uint8_t* scale8, const float* scale2, int64_t o,
                            const uint16_t* A, const uint16_t* B, int r, float s, uint16_t* Y,
-                           float* T_out, uint16_t* Xp, float* Tpart, hipStream_t st);
+                           float* T_out, float* Tpart, hipStream_t st);
 
 }  // namespace qlora

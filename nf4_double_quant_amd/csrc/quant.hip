@@ -20,7 +20,9 @@
 //    DOWN to fp32 gives a threshold th_t with  w > c1·mid_t  <=>  w > th_t
 //    for every fp32 w.  A thread per block builds them once; each weight
 //    then takes a 4-level branch-free binary search in fp32.
-//  * Codes are gathered in LDS and written out as 16-byte stores.
+//  * Codes are packed 8 per 32-bit word (byte j = code j | code j+4 << 4):
+//    the two lanes holding a word's halves merge them with one shuffle, the
+//    words are gathered in LDS and written out as 16-byte stores.
 #include "kernels.h"
 
 namespace qlora {
@@ -55,7 +57,7 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, i
                                                   float* __restrict__ scale2,
                                                   int32_t* __restrict__ flags, Codebook cb) {
   __shared__ __attribute__((aligned(16))) float s_thr[kGroup][16];
-  __shared__ __attribute__((aligned(16))) uint16_t s_codes[kGroupElems / 4];
+  __shared__ __attribute__((aligned(16))) uint32_t s_codes[kGroupElems / 8];
   __shared__ uint32_t s_c1[kGroup];
   __shared__ uint32_t s_red[4];
 
@@ -154,12 +156,16 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, i
     const uint32_t k1 = nf4_search(v[j].y, th);
     const uint32_t k2 = nf4_search(v[j].z, th);
     const uint32_t k3 = nf4_search(v[j].w, th);
-    s_codes[bl * 16 + sub] = (uint16_t)(k0 | (k1 << 4) | (k2 << 8) | (k3 << 12));
+    // lane `sub` holds codes 4·sub..4·sub+3 of the block: low nibbles of a
+    // word for even sub, high nibbles for odd sub
+    const uint32_t half = (k0 | (k1 << 8) | (k2 << 16) | (k3 << 24)) << ((sub & 1) * 4);
+    const uint32_t word = half | (uint32_t)__shfl_xor((int)half, 1, 16);
+    if ((sub & 1) == 0) s_codes[bl * 8 + (sub >> 1)] = word;
   }
   __syncthreads();
 
   // ---- write the group's 8192 code bytes
-  const int64_t code_bytes = (n + 1) / 2;
+  const int64_t code_bytes = (n + 7) / 8 * 4;
   const int64_t cbase = g * (kGroupElems / 2);
   const int64_t off = cbase + (int64_t)t * 32;
   const uint8_t* sc = reinterpret_cast<const uint8_t*>(s_codes) + t * 32;
@@ -175,7 +181,12 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, i
 }
 
 // ------------------------------------------------------------------ dequant
-// Eight weights per thread (one code dword); ŵ = fl32(V[k]·fl32(q8·step)).
+// Code j (0..7) of a packed word.
+__device__ __forceinline__ uint32_t code_of(uint32_t w, int j) {
+  return (w >> (8 * (j & 3) + 4 * (j >> 2))) & 15u;
+}
+
+// Eight weights per thread (one code word); ŵ = fl32(V[k]·fl32(q8·step)).
 template <bool kBf16>
 __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ codes,
                                                  const uint8_t* __restrict__ scale8,
@@ -190,18 +201,10 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ cod
     const int64_t e0 = i * 8;
     const int64_t b = e0 / kBlock;
     const float chat = (float)scale8[b] * scale2[b / kGroup];
-    uint32_t w;
-    if (e0 + 8 <= n) {
-      w = reinterpret_cast<const uint32_t*>(codes)[i];
-    } else {
-      w = 0;
-      const int64_t cb_bytes = (n + 1) / 2;
-      for (int k = 0; k < 4; ++k)
-        if (i * 4 + k < cb_bytes) w |= (uint32_t)codes[i * 4 + k] << (8 * k);
-    }
+    const uint32_t w = reinterpret_cast<const uint32_t*>(codes)[i];
     float r[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) r[k] = s_v[(w >> (4 * k)) & 15u] * chat;
+    for (int k = 0; k < 8; ++k) r[k] = s_v[code_of(w, k)] * chat;
     if (kBf16) {
       uint16_t* o = reinterpret_cast<uint16_t*>(out);
       if (e0 + 8 <= n && ((reinterpret_cast<uintptr_t>(o + e0) & 15) == 0)) {
@@ -253,7 +256,7 @@ __global__ __launch_bounds__(256) void k_dequant_t(const uint8_t* __restrict__ c
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
         const uint32_t w = k < 8 ? w2.x : w2.y;
-        tile[row][q * 16 + k] = bf16_bits(s_v[(w >> (4 * (k & 7))) & 15u] * chat);
+        tile[row][q * 16 + k] = bf16_bits(s_v[code_of(w, k & 7)] * chat);
       }
     }
   }
