@@ -188,13 +188,14 @@ typedef enum {
   QLORA_K_COUNT = 6
 } qlora_kernel_class;
 
-/* Launch timing for benchmarks: between qlora_timing_begin() and
- * qlora_timing_end(), every launch of the library records a pair of HIP
- * events on its own stream around the kernel(s) of its class.
- * qlora_timing_read() waits for those events and returns the summed elapsed
- * milliseconds and the number of launches of one class.  Process-wide, not
- * thread-safe; meant for single-threaded benchmark drivers. */
-int qlora_timing_begin(void);
+/* Launch timing for benchmarks: between qlora_timing_begin(mask) and
+ * qlora_timing_end(), every launch of a class whose bit (1 << class) is set
+ * in `mask` records a pair of HIP events on its own stream around the
+ * kernel(s).  qlora_timing_read() waits for those events and returns the
+ * summed elapsed milliseconds and the number of launches of one class.
+ * Process-wide, not thread-safe; meant for single-threaded benchmark
+ * drivers. */
+int qlora_timing_begin(uint32_t mask);
 int qlora_timing_end(void);
 int qlora_timing_read(int kernel_class, double* total_ms, int64_t* launches);
 

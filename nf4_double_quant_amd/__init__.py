@@ -61,6 +61,7 @@ def lib() -> ctypes.CDLL:
                                    vp, vp, vp, sz, vp]
     L.qlora_linear_bwd.argtypes = [vp, vp, vp, i64, i64, P(_NF4DQ), i64, vp, vp, i64,
                                    ctypes.c_float, vp, vp, vp, vp, sz, vp]
+    L.qlora_timing_begin.argtypes = [ctypes.c_uint32]
     L.qlora_timing_read.argtypes = [i32, P(ctypes.c_double), P(i64)]
     for name in ("qlora_quant_sizes", "qlora_codebook", "qlora_quantize_nf4_dq", "qlora_dequant",
                  "qlora_linear_fwd", "qlora_linear_bwd", "qlora_timing_begin", "qlora_timing_end",
@@ -104,8 +105,10 @@ KERNEL_CLASSES = {"main_gemm": K_MAIN_GEMM, "quantize": K_QUANTIZE, "gemv": K_GE
                   "dequant": K_DEQUANT, "adapter": K_ADAPTER, "grads": K_GRADS}
 
 
-def qlora_timing_begin():
-    _check(lib().qlora_timing_begin(), "qlora_timing_begin")
+def qlora_timing_begin(classes=None):
+    """Start recording launch events for the given kernel classes (default: all)."""
+    mask = 0xFFFFFFFF if classes is None else sum(1 << c for c in classes)
+    _check(lib().qlora_timing_begin(mask), "qlora_timing_begin")
 
 
 def qlora_timing_end():

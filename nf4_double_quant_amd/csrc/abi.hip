@@ -20,61 +20,43 @@ inline int64_t up(int64_t a) { return cdiv(a, kAlign) * kAlign; }
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 inline int64_t clampi(int64_t v, int64_t lo, int64_t hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
-// Split counts: enough workgroups to cover the 256 CUs about twice.
-int64_t splits_nt(int64_t M, int64_t N, int64_t K) {
-  const int64_t tiles = cdiv(M, 64) * cdiv(N, 64);
-  if (tiles == 0) return 1;
-  return clampi(cdiv(512, tiles), 1, clampi(cdiv(K, 64), 1, 16));
-}
-int64_t splits_tn(int64_t P, int64_t Q, int64_t Mtok) {
-  const int64_t tiles = P <= 64 ? cdiv(P, 64) * cdiv(Q, 128) : cdiv(P, 128) * cdiv(Q, 64);
-  if (tiles == 0) return 1;
-  return clampi(cdiv(512, tiles), 1, clampi(cdiv(Mtok, 64), 1, 32));
-}
-
 struct FwdLayout {
-  bool gemv;                                   // few-token path
-  int64_t At, Bt, Tpart, sT, total;  // byte offsets into the workspace
-  int64_t sT_splits;
+  bool gemv;               // few-token path
+  int64_t Tpart, sT, total;  // byte offsets into the workspace
+  int64_t t_splits;
 };
 FwdLayout fwd_layout(int64_t M, int64_t d, int64_t o, int64_t r) {
+  (void)o;
   FwdLayout L{};
   int64_t off = 0;
   L.gemv = M <= kGemvMaxTokens;
-  if (L.gemv) {
-    L.sT_splits = gemv_tsplits(d);
-    L.Tpart = off; off += up(4 * L.sT_splits * M * r);
-  } else {
-    L.sT_splits = r > 0 ? splits_nt(M, r, d) : 0;
-    L.At = off;    off += up(2 * r * d);
-    L.Bt = off;    off += up(2 * o * r);
-    L.Tpart = off; off += up(4 * L.sT_splits * M * r);
-    L.sT = off;    off += up(2 * M * r);
+  L.t_splits = L.gemv ? gemv_tsplits(d) : rank_down_splits(d);
+  L.Tpart = off; off += up(4 * L.t_splits * M * r);
+  if (!L.gemv) {
+    L.sT = off;  off += up(2 * M * r);
   }
   L.total = off;
   return L;
 }
 
 struct BwdLayout {
-  int64_t At, Tpart, sT, Upart, sU, dApart, dBpart, total;
-  int64_t t_splits, u_splits, a_splits, b_splits;
+  int64_t Tpart, sT, Upart, sU, dApart, dBpart, total;
+  int64_t t_splits, u_splits, g_splits;
 };
 BwdLayout bwd_layout(int64_t M, int64_t d, int64_t o, int64_t r) {
   BwdLayout L{};
   int64_t off = 0;
   if (r > 0) {
-    L.t_splits = splits_nt(M, r, d);
-    L.u_splits = splits_nt(M, r, o);
-    L.a_splits = splits_tn(d, r, M);
-    L.b_splits = splits_tn(r, o, M);
+    L.t_splits = rank_down_splits(d);
+    L.u_splits = rank_down_splits(o);
+    L.g_splits = rank_grad_splits(M);
   }
-  L.At = off;     off += up(2 * r * d);
   L.Tpart = off;  off += up(4 * L.t_splits * M * r);
   L.sT = off;     off += up(2 * M * r);
   L.Upart = off;  off += up(4 * L.u_splits * M * r);
   L.sU = off;     off += up(2 * M * r);
-  L.dApart = off; off += up(4 * L.a_splits * d * r);
-  L.dBpart = off; off += up(4 * L.b_splits * r * o);
+  L.dApart = off; off += up(4 * L.g_splits * d * r);
+  L.dBpart = off; off += up(4 * L.g_splits * r * o);
   L.total = off;
   return L;
 }
@@ -91,6 +73,7 @@ int device_status() {
 // Event pairs recorded around launches while timing is on (diagnostics only).
 struct LaunchTimer {
   bool on = false;
+  uint32_t mask = 0;
   std::vector<std::pair<hipEvent_t, hipEvent_t>> ev[QLORA_K_COUNT];
   void clear() {
     for (auto& v : ev) {
@@ -106,7 +89,7 @@ LaunchTimer g_timer;
 
 template <class F>
 hipError_t timed(int cls, hipStream_t st, F&& f) {
-  if (!g_timer.on) return f();
+  if (!g_timer.on || !((g_timer.mask >> cls) & 1u)) return f();
   hipEvent_t a, b;
   if (hipEventCreate(&a) != hipSuccess) return hipErrorUnknown;
   if (hipEventCreate(&b) != hipSuccess) {
@@ -189,8 +172,9 @@ const char* qlora_strerror(int status) {
 
 const char* qlora_version(void) { return "qlora-mi355x 0.1.0 (gfx950)"; }
 
-int qlora_timing_begin(void) {
+int qlora_timing_begin(uint32_t mask) {
   g_timer.clear();
+  g_timer.mask = mask;
   g_timer.on = true;
   return QLORA_OK;
 }
@@ -258,10 +242,7 @@ int qlora_linear_fwd(const qlora_bf16* X, int64_t M, int64_t d, const qlora_nf4d
   if ((st = device_status())) return st;
   hipStream_t hs = (hipStream_t)stream;
   char* w = static_cast<char*>(ws);
-  uint16_t* At = reinterpret_cast<uint16_t*>(w + L.At);
-  uint16_t* Bt = reinterpret_cast<uint16_t*>(w + L.Bt);
   float* Tpart = reinterpret_cast<float*>(w + L.Tpart);
-  uint16_t* sT = reinterpret_cast<uint16_t*>(w + L.sT);
   const bool lora = r > 0 && s != 0.0f;
 
   if (L.gemv) {
@@ -270,19 +251,16 @@ int qlora_linear_fwd(const qlora_bf16* X, int64_t M, int64_t d, const qlora_nf4d
                            T_out, Tpart, hs));
     return QLORA_OK;
   }
+  uint16_t* sT = reinterpret_cast<uint16_t*>(w + L.sT);
   if (r > 0 && (lora || T_out != nullptr)) {
-    // T = X·A as X·(Aᵀ)ᵀ with split-K over d
-    QL_RUN(QLORA_K_ADAPTER, hs, launch_transpose_bf16(A, d, r, At, hs));
-    GemmArgs g{};
-    g.A = X; g.lda = d; g.B = At; g.ldb = d;
-    g.M = M; g.N = r; g.K = d; g.C = Tpart; g.ldc = r;
-    QL_RUN(QLORA_K_ADAPTER, hs, launch_gemm_nt_splitk(g, (int)L.sT_splits, hs));
-    QL_RUN(QLORA_K_ADAPTER, hs, launch_reduce_planes(Tpart, (int)L.sT_splits, M * r, M, r, r, T_out, r,
-                                lora ? sT : nullptr, r, s, hs));
+    // T = X·A as split-K planes, summed into T_out (fp32) and s·T (bf16)
+    QL_RUN(QLORA_K_ADAPTER, hs, launch_rank_down(false, X, M, d, A, (int)r, Tpart, hs));
+    QL_RUN(QLORA_K_ADAPTER, hs,
+           launch_reduce_planes(Tpart, (int)L.t_splits, M * r, M * r, T_out, lora ? sT : nullptr,
+                                s, hs));
   }
-  if (lora) QL_RUN(QLORA_K_ADAPTER, hs, launch_transpose_bf16(B, r, o, Bt, hs));
   QL_RUN(QLORA_K_MAIN_GEMM, hs,
-         launch_qgemm(false, X, d, W->codes, W->scale8, W->scale2, d, sT, r, Bt, r, M, o, d,
+         launch_qgemm(false, X, d, W->codes, W->scale8, W->scale2, d, sT, r, B, o, M, o, d,
                       lora ? r : 0, Y, o, hs));
   return QLORA_OK;
 }
@@ -314,56 +292,38 @@ int qlora_linear_bwd(const qlora_bf16* dY, const qlora_bf16* X, const float* T, 
     return QLORA_OK;
   }
   char* w = static_cast<char*>(ws);
-  uint16_t* At = reinterpret_cast<uint16_t*>(w + L.At);
   float* Tpart = reinterpret_cast<float*>(w + L.Tpart);
   uint16_t* sT = reinterpret_cast<uint16_t*>(w + L.sT);
   float* Upart = reinterpret_cast<float*>(w + L.Upart);
   uint16_t* sU = reinterpret_cast<uint16_t*>(w + L.sU);
   float* dApart = reinterpret_cast<float*>(w + L.dApart);
   float* dBpart = reinterpret_cast<float*>(w + L.dBpart);
+  const bool lora = r > 0 && s != 0.0f;
 
   if (r > 0) {
-    // s·T in bf16 (operand of dB = (sT)ᵀ·dY)
+    // s·T in bf16, the operand of dB = (s·T)ᵀ·dY
     if (T != nullptr) {
       QL_RUN(QLORA_K_ADAPTER, hs, launch_scale_to_bf16(T, M * r, s, sT, hs));
     } else {
-      QL_RUN(QLORA_K_ADAPTER, hs, launch_transpose_bf16(A, d, r, At, hs));
-      GemmArgs g{};
-      g.A = X; g.lda = d; g.B = At; g.ldb = d;
-      g.M = M; g.N = r; g.K = d; g.C = Tpart; g.ldc = r;
-      QL_RUN(QLORA_K_ADAPTER, hs, launch_gemm_nt_splitk(g, (int)L.t_splits, hs));
-      QL_RUN(QLORA_K_ADAPTER, hs, launch_reduce_planes(Tpart, (int)L.t_splits, M * r, M, r, r, nullptr, r, sT, r, s, hs));
+      QL_RUN(QLORA_K_ADAPTER, hs, launch_rank_down(false, X, M, d, A, (int)r, Tpart, hs));
+      QL_RUN(QLORA_K_ADAPTER, hs,
+             launch_reduce_planes(Tpart, (int)L.t_splits, M * r, M * r, nullptr, sT, s, hs));
     }
-    // s·U = s·dY·Bᵀ; B[r][o] is already the K-major operand
-    {
-      GemmArgs g{};
-      g.A = dY; g.lda = o; g.B = B; g.ldb = o;
-      g.M = M; g.N = r; g.K = o; g.C = Upart; g.ldc = r;
-      QL_RUN(QLORA_K_ADAPTER, hs, launch_gemm_nt_splitk(g, (int)L.u_splits, hs));
-      QL_RUN(QLORA_K_ADAPTER, hs, launch_reduce_planes(Upart, (int)L.u_splits, M * r, M, r, r, nullptr, r, sU, r, s, hs));
-    }
-    // dA = Xᵀ·(s·U)   [d][r], reduction over tokens
-    {
-      GemmArgs g{};
-      g.A = X; g.lda = d; g.B = sU; g.ldb = r;
-      g.M = d; g.N = r; g.K = M; g.C = dApart; g.ldc = r;
-      QL_RUN(QLORA_K_GRADS, hs, launch_gemm_tn_splitk(g, (int)L.a_splits, hs));
-      QL_RUN(QLORA_K_GRADS, hs, launch_reduce_planes(dApart, (int)L.a_splits, d * r, d, r, r, nullptr, r, dA, r, 1.0f, hs));
-    }
-    // dB = (s·T)ᵀ·dY  [r][o]
-    {
-      GemmArgs g{};
-      g.A = sT; g.lda = r; g.B = dY; g.ldb = o;
-      g.M = r; g.N = o; g.K = M; g.C = dBpart; g.ldc = o;
-      QL_RUN(QLORA_K_GRADS, hs, launch_gemm_tn_splitk(g, (int)L.b_splits, hs));
-      QL_RUN(QLORA_K_GRADS, hs, launch_reduce_planes(dBpart, (int)L.b_splits, r * o, r, o, o, nullptr, o, dB, o, 1.0f, hs));
-    }
+    // s·U = s·dY·Bᵀ (B [r][o] is the K-major operand)
+    QL_RUN(QLORA_K_ADAPTER, hs, launch_rank_down(true, dY, M, o, B, (int)r, Upart, hs));
+    QL_RUN(QLORA_K_ADAPTER, hs,
+           launch_reduce_planes(Upart, (int)L.u_splits, M * r, M * r, nullptr, sU, s, hs));
+    // dA = Xᵀ·(s·U) [d][r] and dB = (s·T)ᵀ·dY [r][o], reductions over the tokens
+    QL_RUN(QLORA_K_GRADS, hs, launch_rank_grad(true, X, d, sU, (int)r, M, dApart, hs));
+    QL_RUN(QLORA_K_GRADS, hs, launch_rank_grad(false, dY, o, sT, (int)r, M, dBpart, hs));
+    QL_RUN(QLORA_K_GRADS, hs,
+           launch_reduce_planes(dApart, (int)L.g_splits, d * r, d * r, nullptr, dA, 1.0f, hs));
+    QL_RUN(QLORA_K_GRADS, hs,
+           launch_reduce_planes(dBpart, (int)L.g_splits, r * o, r * o, nullptr, dB, 1.0f, hs));
   }
   if (dX != nullptr) {
-    const bool lora = r > 0 && s != 0.0f;
-    if (lora && T != nullptr) QL_RUN(QLORA_K_ADAPTER, hs, launch_transpose_bf16(A, d, r, At, hs));
     QL_RUN(QLORA_K_MAIN_GEMM, hs,
-           launch_qgemm(true, dY, o, W->codes, W->scale8, W->scale2, d, sU, r, At, d, M, d, o,
+           launch_qgemm(true, dY, o, W->codes, W->scale8, W->scale2, d, sU, r, A, r, M, d, o,
                         lora ? r : 0, dX, d, hs));
   }
   return QLORA_OK;

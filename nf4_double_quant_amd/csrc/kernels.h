@@ -6,41 +6,37 @@
 
 namespace qlora {
 
-struct GemmArgs {
-  const uint16_t* A;  int64_t lda;   // K-major: [M][lda]; M-major: [K][lda]
-  const uint16_t* B;  int64_t ldb;   // K-major: [N][ldb]; M-major: [K][ldb]
-  const uint16_t* A2; int64_t lda2;  // adapter segment, K-major [M][K2]
-  const uint16_t* B2; int64_t ldb2;  // adapter segment, K-major [N][K2]
-  int64_t M, N, K, K2;
-  void* C; int64_t ldc;              // bf16 [M][ldc], or fp32 planes [z][M][ldc]
-  int64_t k_split;                   // main-segment K handled per blockIdx.z
-  int64_t plane;                     // fp32 elements between partial planes
-};
 
 hipError_t launch_quantize(const float* W, int64_t n, uint8_t* codes, uint8_t* scale8,
                            float* scale2, int32_t* flags, hipStream_t st);
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scale8, const float* scale2,
                           int64_t n, bool bf16, void* out, hipStream_t st);
-hipError_t launch_dequant_t(const uint8_t* codes, const uint8_t* scale8, const float* scale2,
-                            int64_t o, int64_t d, uint16_t* WT, hipStream_t st);
 
-hipError_t launch_gemm_nt_bf16(const GemmArgs& a, hipStream_t st);
 
 // Fused NF4 dequant-GEMM: C = A·Ŵ (+ A2·B2) with Ŵ from the quantized Wq[o][d].
-// trans_w = false: forward, C[M][N=o] = A[M][K=d]·Wqᵀ, B2 = Bᵀ [N][K2].
-// trans_w = true:  backward, C[M][N=d] = A[M][K=o]·Wq, B2 = Aᵀ [K2][N].
+// trans_w = false: forward, C[M][N=o] = A[M][K=d]·Wqᵀ + A2·B2, B2 = B [K2][N].
+// trans_w = true:  backward, C[M][N=d] = A[M][K=o]·Wq + A2·B2ᵀ, B2 = A [N][K2].
 hipError_t launch_qgemm(bool trans_w, const uint16_t* A, int64_t lda, const uint8_t* codes,
                         const uint8_t* scale8, const float* scale2, int64_t d,
                         const uint16_t* A2, int64_t lda2, const uint16_t* B2, int64_t ldb2,
                         int64_t M, int64_t N, int64_t K, int64_t K2, uint16_t* C, int64_t ldc,
                         hipStream_t st);
-hipError_t launch_gemm_nt_splitk(const GemmArgs& a, int splits, hipStream_t st);
-hipError_t launch_gemm_tn_splitk(const GemmArgs& a, int splits, hipStream_t st);
-hipError_t launch_reduce_planes(const float* part, int splits, int64_t plane, int64_t rows,
-                                int64_t cols, int64_t ldp, float* out_f32, int64_t ldf,
-                                uint16_t* out_bf16, int64_t ldb, float scale, hipStream_t st);
-hipError_t launch_transpose_bf16(const uint16_t* src, int64_t R, int64_t C, uint16_t* dst,
-                                 hipStream_t st);
+
+// Rank-r products (split planes, summed by launch_reduce_planes):
+// part[z][M][r] = P[M][K-slice z]·Q with Q = Qsrc[K][r], or Q = Qsrc[r][K]ᵀ
+// when q_rowmajor_k; rank_down_splits(K) planes.
+int rank_down_splits(int64_t K);
+hipError_t launch_rank_down(bool q_rowmajor_k, const uint16_t* P, int64_t M, int64_t K,
+                            const uint16_t* Q, int r, float* part, hipStream_t st);
+// part[z] = Σ_{m in token slice z} big[m][p]·small[m][j], stored [P][r] when
+// out_pj, else [r][P]; rank_grad_splits(M) planes.
+int rank_grad_splits(int64_t M);
+hipError_t launch_rank_grad(bool out_pj, const uint16_t* big, int64_t P, const uint16_t* small,
+                            int r, int64_t M, float* part, hipStream_t st);
+
+// Contiguous split-K planes [splits][count] (count % 4 == 0) -> their sum.
+hipError_t launch_reduce_planes(const float* part, int splits, int64_t plane, int64_t count,
+                                float* out_f32, uint16_t* out_bf16, float scale, hipStream_t st);
 hipError_t launch_scale_to_bf16(const float* x, int64_t n, float scale, uint16_t* y,
                                 hipStream_t st);
 hipError_t launch_fill_zero_bf16(uint16_t* y, int64_t n, hipStream_t st);

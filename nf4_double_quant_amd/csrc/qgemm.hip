@@ -19,10 +19,13 @@
 //  * backward: a block is 64 consecutive n of one k, so the tile is stored
 //    [k][n] (rows padded to 544 bytes) and the MFMA B operand is gathered
 //    with ds_read_b64_tr_b16, four k of one n per lane per read.
-// The adapter term is one (or a few) extra k-steps over [s·T ‖ Bᵀ] or
-// [s·U ‖ Aᵀ], accumulated into the same registers, so Y and dX are rounded
-// to bf16 once.  Workgroups are numbered so that each XCD (round-robin
+// The adapter term is one (or a few) extra k-steps over [s·T ‖ B] or
+// [s·U ‖ A], accumulated into the same registers, so Y and dX are rounded
+// to bf16 once.  B [r][o] is n-major like the backward weight tile and A
+// [d][r] k-major like the forward one, so neither needs a transposed copy.  Workgroups are numbered so that each XCD (round-robin
 // dispatch over 8) works on a contiguous band of output tiles.
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace qlora {
@@ -85,7 +88,7 @@ struct QGemmArgs {
   const uint8_t* codes; const uint8_t* scale8; const float* scale2;   // Wq[o][d]
   int64_t d;                         // row length of Wq
   const uint16_t* A2; int64_t lda2;  // adapter activations [M][K2]
-  const uint16_t* B2; int64_t ldb2;  // forward: Bᵀ [N][K2]; backward: Aᵀ [K2][N]
+  const uint16_t* B2; int64_t ldb2;  // forward: B [K2][N]; backward: A [N][K2]
   int64_t M, N, K, K2;
   uint16_t* C; int64_t ldc;
   Codebook cb;
@@ -93,6 +96,7 @@ struct QGemmArgs {
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr uint32_t kOobOff = 0x7FFFFFF0u;   // an offset every descriptor rejects
 
 // Range-checked buffer descriptor (gfx9 family): loads past `bytes` read 0,
 // stores past it are dropped.
@@ -198,7 +202,10 @@ __global__ __launch_bounds__(kThreads) void k_qgemm(QGemmArgs p) {
   // The weight fragment is the MFMA's first operand and the activation
   // fragment its second, so each lane accumulates 4 consecutive output
   // columns of one output row (the epilogue stores 8 bytes at a time).
-  auto compute = [&](const uint16_t* sa, const uint16_t* sb) {
+  // kBTr: the weight-side tile is [k][n] (read transposed) instead of [n][k].
+  auto compute = [&](auto btr_tag, const uint16_t* sa, const uint16_t* sb) {
+    constexpr bool kBTr = decltype(btr_tag)::value;
+    constexpr int TSTR = kBN + 16;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       bf16x8 a[4], b[4];
@@ -210,15 +217,15 @@ __global__ __launch_bounds__(kThreads) void k_qgemm(QGemmArgs p) {
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        if (!kTransW) {
+        if (!kBTr) {
           const int row = wn * 128 + j * 32 + (lane & 31);
           b[j] = *reinterpret_cast<const bf16x8*>(sb + row * kBK + ((ch ^ swz8(row)) << 3));
         } else {
           const int g = lane >> 4, s = lane & 15;
           const int col = wn * 128 + j * 32 + 16 * (g & 1) + 4 * (s & 3);
           const int kr = kk * 16 + 8 * (g >> 1) + (s >> 2);
-          const s16x4 lo = lds_tr(sb + kr * BSTR + col);
-          const s16x4 hi = lds_tr(sb + (kr + 4) * BSTR + col);
+          const s16x4 lo = lds_tr(sb + kr * TSTR + col);
+          const s16x4 hi = lds_tr(sb + (kr + 4) * TSTR + col);
           const s16x8 bv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           b[j] = __builtin_bit_cast(bf16x8, bv);
         }
@@ -230,6 +237,8 @@ __global__ __launch_bounds__(kThreads) void k_qgemm(QGemmArgs p) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
     }
   };
+  using WTag = std::integral_constant<bool, kTransW>;
+  using ATag = std::integral_constant<bool, !kTransW>;
 
   // ---- main loop over the quantized weight: one branch-free block per k-step
   if (nk > 0) {
@@ -253,7 +262,7 @@ __global__ __launch_bounds__(kThreads) void k_qgemm(QGemmArgs p) {
       load_codes(s + 2, refill);
       uint4 dq[8];
       dequant(next, dq);
-      compute(sA[cur], sB[cur]);
+      compute(WTag{}, sA[cur], sB[cur]);
       store_a(sA[cur ^ 1]);
       store_w(dq, sB[cur ^ 1]);
       __syncthreads();
@@ -266,11 +275,14 @@ __global__ __launch_bounds__(kThreads) void k_qgemm(QGemmArgs p) {
     if (s < nk) iteration(s, r0, r1);
   }
 
-  // ---- adapter k-steps: [s·T ‖ Bᵀ] (forward) or [s·U ‖ Aᵀ] (backward)
+  // ---- adapter k-steps: [s·T ‖ B] (forward, B is [r][N]: an n-major tile
+  // read transposed) or [s·U ‖ A] (backward, A is [N][r]: a k-major tile)
   if (nk2 > 0) {
+    constexpr int TSTR = kBN + 16;
+    uint16_t* sb = &sB[0][0];          // spans both stages (up to 34 KB used)
     const Rsrc r2 = rsrc(p.A2 + m0 * p.lda2, mrows * p.lda2 * 2);
-    const Rsrc rb2 = kTransW ? rsrc(p.B2, p.K2 * p.ldb2 * 2)
-                             : rsrc(p.B2 + n0 * p.ldb2, min((int64_t)kBN, p.N - n0) * p.ldb2 * 2);
+    const Rsrc rb2 = !kTransW ? rsrc(p.B2, p.K2 * p.ldb2 * 2)
+                              : rsrc(p.B2 + n0 * p.ldb2, min((int64_t)kBN, p.N - n0) * p.ldb2 * 2);
     for (int ls = 0; ls < nk2; ++ls) {
       const int64_t k0 = (int64_t)ls * kBK;
       uint4 rb[8];
@@ -279,29 +291,28 @@ __global__ __launch_bounds__(kThreads) void k_qgemm(QGemmArgs p) {
         const int c = i * kThreads + t;
         const int row = c >> 3;
         const int64_t gk = k0 + (c & 7) * 8;
-        const uint4 z = make_uint4(0, 0, 0, 0);
-        ra[i] = gk < p.K2 ? bload16(r2, (uint32_t)((row * p.lda2 + gk) * 2)) : z;
-        if (!kTransW) {
-          rb[i] = gk < p.K2 ? bload16(rb2, (uint32_t)((row * p.ldb2 + gk) * 2)) : z;
-        } else {
+        ra[i] = bload16(r2, gk < p.K2 ? (uint32_t)((row * p.lda2 + gk) * 2) : kOobOff);
+        if (kTransW) {   // A rows n, k-major
+          rb[i] = bload16(rb2, gk < p.K2 ? (uint32_t)((row * p.ldb2 + gk) * 2) : kOobOff);
+        } else {         // B rows k, n-major
           const int kr = c >> 5;
           const int64_t gk2 = k0 + kr, gn = n0 + (c & 31) * 8;
-          rb[i] = (gk2 < p.K2 && gn < p.N) ? bload16(rb2, (uint32_t)((gk2 * p.ldb2 + gn) * 2)) : z;
+          rb[i] = bload16(rb2, (gk2 < p.K2 && gn < p.N) ? (uint32_t)((gk2 * p.ldb2 + gn) * 2) : kOobOff);
         }
       }
       store_a(sA[0]);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int c = i * kThreads + t;
-        if (!kTransW) {
+        if (kTransW) {
           const int row = c >> 3, ch = c & 7;
-          *reinterpret_cast<uint4*>(sB[0] + row * kBK + ((ch ^ swz8(row)) << 3)) = rb[i];
+          *reinterpret_cast<uint4*>(sb + row * kBK + ((ch ^ swz8(row)) << 3)) = rb[i];
         } else {
-          *reinterpret_cast<uint4*>(sB[0] + (c >> 5) * BSTR + (c & 31) * 8) = rb[i];
+          *reinterpret_cast<uint4*>(sb + (c >> 5) * TSTR + (c & 31) * 8) = rb[i];
         }
       }
       __syncthreads();
-      compute(sA[0], sB[0]);
+      compute(ATag{}, sA[0], sb);
       __syncthreads();
     }
   }

@@ -37,26 +37,44 @@ __device__ __forceinline__ float round_down_f32(double p) {
   return f;
 }
 
-// Number of thresholds strictly below w (= the NF4 code), thresholds ascending.
-__device__ __forceinline__ uint32_t nf4_search(float w, const float (&t)[16]) {
-  const bool b3 = w > t[7];
-  const bool b2 = w > (b3 ? t[11] : t[3]);
-  const float t1 = b3 ? (b2 ? t[13] : t[9]) : (b2 ? t[5] : t[1]);
+// Number of thresholds strictly below w (= the NF4 code); thresholds
+// t0..t14 ascending in a.x..d.z.  A 4-level search on register values.
+__device__ __forceinline__ uint32_t nf4_search(float w, float4 a, float4 b, float4 c, float4 d) {
+  const bool b3 = w > b.w;                                   // t7
+  const bool b2 = w > (b3 ? c.w : a.w);                      // t11 | t3
+  const float t1 = b3 ? (b2 ? d.y : c.y) : (b2 ? b.y : a.y); // t13 t9 t5 t1
   const bool b1 = w > t1;
-  const float t0 = b3 ? (b2 ? (b1 ? t[14] : t[12]) : (b1 ? t[10] : t[8]))
-                      : (b2 ? (b1 ? t[6] : t[4]) : (b1 ? t[2] : t[0]));
-  const bool b0 = w > t0;
+  const float lo = b1 ? (b2 ? b.z : a.z) : (b2 ? b.x : a.x); // t6 t2 t4 t0
+  const float hi = b1 ? (b2 ? d.z : c.z) : (b2 ? d.x : c.x); // t14 t10 t12 t8
+  const bool b0 = w > (b3 ? hi : lo);
   return ((uint32_t)b3 << 3) | ((uint32_t)b2 << 2) | ((uint32_t)b1 << 1) | (uint32_t)b0;
 }
 
+// max over the 16 lanes of a DPP row (rotations by 8, 4, 2, 1)
+__device__ __forceinline__ uint32_t row_max16(uint32_t a) {
+  a = max(a, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, 0x128, 0xF, 0xF, false));
+  a = max(a, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, 0x124, 0xF, 0xF, false));
+  a = max(a, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, 0x122, 0xF, 0xF, false));
+  a = max(a, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, 0x121, 0xF, 0xF, false));
+  return a;
+}
+
 __device__ __forceinline__ uint32_t abs_bits(float x) { return __float_as_uint(x) & 0x7FFFFFFFu; }
+
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+__device__ __forceinline__ Rsrc rsrc(const void* base, int64_t bytes) {
+  const int64_t cap = 0x7FFFFFF0;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                           (int)(bytes < 0 ? 0 : (bytes > cap ? cap : bytes)),
+                                           0x00020000);
+}
 
 __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, int64_t n,
                                                   uint8_t* __restrict__ codes,
                                                   uint8_t* __restrict__ scale8,
                                                   float* __restrict__ scale2,
                                                   int32_t* __restrict__ flags, Codebook cb) {
-  __shared__ __attribute__((aligned(16))) float s_thr[kGroup][16];
+  __shared__ __attribute__((aligned(16))) float4 s_thr[kGroup][4];
   __shared__ __attribute__((aligned(16))) uint32_t s_codes[kGroupElems / 8];
   __shared__ uint32_t s_c1[kGroup];
   __shared__ uint32_t s_red[4];
@@ -67,29 +85,20 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, i
   const int64_t base = g * kGroupElems;
   const int64_t nb = (n + kBlock - 1) / kBlock;
 
-  // ---- load the group (zeros past n) and take per-block absmax
+  // ---- load the group (reads past n return 0) and take per-block absmax
+  const Rsrc rw = rsrc(W + base, (min((int64_t)kGroupElems, n - base)) * 4);
   float4 v[16];
-  uint32_t bad = 0;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     const int bl = wave * 64 + j * 4 + quad;
-    const int64_t e = base + (int64_t)bl * kBlock + sub * 4;
-    if (e + 4 <= n) {
-      v[j] = *reinterpret_cast<const float4*>(W + e);
-    } else {
-      v[j].x = e + 0 < n ? W[e + 0] : 0.0f;
-      v[j].y = e + 1 < n ? W[e + 1] : 0.0f;
-      v[j].z = e + 2 < n ? W[e + 2] : 0.0f;
-      v[j].w = e + 3 < n ? W[e + 3] : 0.0f;
-    }
+    const int off = (bl * kBlock + sub * 4) * 4;
+    v[j] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 0));
   }
+  uint32_t bad = 0;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     uint32_t a = max(max(abs_bits(v[j].x), abs_bits(v[j].y)), max(abs_bits(v[j].z), abs_bits(v[j].w)));
-    a = max(a, (uint32_t)__shfl_xor((int)a, 8, 16));
-    a = max(a, (uint32_t)__shfl_xor((int)a, 4, 16));
-    a = max(a, (uint32_t)__shfl_xor((int)a, 2, 16));
-    a = max(a, (uint32_t)__shfl_xor((int)a, 1, 16));
+    a = row_max16(a);
     bad |= (a >= 0x7F800000u);
     if (sub == 0) s_c1[wave * 64 + j * 4 + quad] = a;
   }
@@ -133,11 +142,10 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, i
       for (int i = 0; i < 15; ++i) th[i] = round_down_f32((double)c1 * cb.mid[i]);
       th[15] = 0.0f;
     }
-    float4* dst = reinterpret_cast<float4*>(&s_thr[t][0]);
-    dst[0] = make_float4(th[0], th[1], th[2], th[3]);
-    dst[1] = make_float4(th[4], th[5], th[6], th[7]);
-    dst[2] = make_float4(th[8], th[9], th[10], th[11]);
-    dst[3] = make_float4(th[12], th[13], th[14], th[15]);
+    s_thr[t][0] = make_float4(th[0], th[1], th[2], th[3]);
+    s_thr[t][1] = make_float4(th[4], th[5], th[6], th[7]);
+    s_thr[t][2] = make_float4(th[8], th[9], th[10], th[11]);
+    s_thr[t][3] = make_float4(th[12], th[13], th[14], th[15]);
   }
   __syncthreads();
 
@@ -145,38 +153,27 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, i
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     const int bl = wave * 64 + j * 4 + quad;
-    const float4* src = reinterpret_cast<const float4*>(&s_thr[bl][0]);
-    float th[16];
-    const float4 t0 = src[0], t1 = src[1], t2 = src[2], t3 = src[3];
-    th[0] = t0.x; th[1] = t0.y; th[2] = t0.z; th[3] = t0.w;
-    th[4] = t1.x; th[5] = t1.y; th[6] = t1.z; th[7] = t1.w;
-    th[8] = t2.x; th[9] = t2.y; th[10] = t2.z; th[11] = t2.w;
-    th[12] = t3.x; th[13] = t3.y; th[14] = t3.z; th[15] = t3.w;
-    const uint32_t k0 = nf4_search(v[j].x, th);
-    const uint32_t k1 = nf4_search(v[j].y, th);
-    const uint32_t k2 = nf4_search(v[j].z, th);
-    const uint32_t k3 = nf4_search(v[j].w, th);
+    const float4 ta = s_thr[bl][0], tb = s_thr[bl][1], tc = s_thr[bl][2], td = s_thr[bl][3];
+    const uint32_t k0 = nf4_search(v[j].x, ta, tb, tc, td);
+    const uint32_t k1 = nf4_search(v[j].y, ta, tb, tc, td);
+    const uint32_t k2 = nf4_search(v[j].z, ta, tb, tc, td);
+    const uint32_t k3 = nf4_search(v[j].w, ta, tb, tc, td);
     // lane `sub` holds codes 4·sub..4·sub+3 of the block: low nibbles of a
-    // word for even sub, high nibbles for odd sub
+    // word for even sub, high nibbles for odd sub; neighbours merge by DPP
     const uint32_t half = (k0 | (k1 << 8) | (k2 << 16) | (k3 << 24)) << ((sub & 1) * 4);
-    const uint32_t word = half | (uint32_t)__shfl_xor((int)half, 1, 16);
-    if ((sub & 1) == 0) s_codes[bl * 8 + (sub >> 1)] = word;
+    const uint32_t other = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)half, 0xB1, 0xF, 0xF, false);
+    if ((sub & 1) == 0) s_codes[bl * 8 + (sub >> 1)] = half | other;
   }
   __syncthreads();
 
-  // ---- write the group's 8192 code bytes
+  // ---- write the group's 8192 code bytes (stores past the buffer are dropped)
   const int64_t code_bytes = (n + 7) / 8 * 4;
   const int64_t cbase = g * (kGroupElems / 2);
-  const int64_t off = cbase + (int64_t)t * 32;
-  const uint8_t* sc = reinterpret_cast<const uint8_t*>(s_codes) + t * 32;
-  if (off + 32 <= code_bytes) {
-    uint4* dst = reinterpret_cast<uint4*>(codes + off);
-    dst[0] = reinterpret_cast<const uint4*>(sc)[0];
-    dst[1] = reinterpret_cast<const uint4*>(sc)[1];
-  } else {
-    for (int i = 0; i < 32; ++i)
-      if (off + i < code_bytes) codes[off + i] = sc[i];
-  }
+  const Rsrc rcod = rsrc(codes + cbase, code_bytes - cbase);
+  const uint4 a = reinterpret_cast<const uint4*>(s_codes)[t * 2];
+  const uint4 b = reinterpret_cast<const uint4*>(s_codes)[t * 2 + 1];
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) int, a), rcod, t * 32, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) int, b), rcod, t * 32 + 16, 0, 0);
   if (bad && flags != nullptr) flags[0] = flags[0] | 1;
 }
 
@@ -231,58 +228,6 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ cod
   }
 }
 
-// Transposed bf16 dequant of a row-major Wq[o][d] (d % 64 == 0) into WT[d][o],
-// the K-major operand of the input-gradient product.  One 64×64 tile (64 rows,
-// one block each) per workgroup, transposed through LDS.
-__global__ __launch_bounds__(256) void k_dequant_t(const uint8_t* __restrict__ codes,
-                                                   const uint8_t* __restrict__ scale8,
-                                                   const float* __restrict__ scale2, int64_t o,
-                                                   int64_t d, uint16_t* __restrict__ WT,
-                                                   Codebook cb) {
-  __shared__ uint16_t tile[64][66];
-  __shared__ float s_v[16];
-  if (threadIdx.x < 16) s_v[threadIdx.x] = cb.v[threadIdx.x];
-  __syncthreads();
-  const int t = threadIdx.x;
-  const int64_t o0 = (int64_t)blockIdx.y * 64, d0 = (int64_t)blockIdx.x * 64;
-  {
-    const int row = t >> 2, q = t & 3;
-    const int64_t orow = o0 + row;
-    if (orow < o) {
-      const int64_t e0 = orow * d + d0 + q * 16;
-      const int64_t b = e0 / kBlock;
-      const float chat = (float)scale8[b] * scale2[b / kGroup];
-      const uint2 w2 = *reinterpret_cast<const uint2*>(codes + e0 / 2);
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const uint32_t w = k < 8 ? w2.x : w2.y;
-        tile[row][q * 16 + k] = bf16_bits(s_v[code_of(w, k & 7)] * chat);
-      }
-    }
-  }
-  __syncthreads();
-  {
-    const int col = t >> 2, q = t & 3;   // output row d0+col, o range o0+16q..
-    const int64_t drow = d0 + col;
-    uint16_t vals[16];
-#pragma unroll
-    for (int k = 0; k < 16; ++k) vals[k] = tile[q * 16 + k][col];
-    uint16_t* dst = WT + drow * o + o0 + q * 16;
-    if (o0 + q * 16 + 16 <= o && (o % 8) == 0) {
-      uint4 a, b;
-      a.x = vals[0] | ((uint32_t)vals[1] << 16);   a.y = vals[2] | ((uint32_t)vals[3] << 16);
-      a.z = vals[4] | ((uint32_t)vals[5] << 16);   a.w = vals[6] | ((uint32_t)vals[7] << 16);
-      b.x = vals[8] | ((uint32_t)vals[9] << 16);   b.y = vals[10] | ((uint32_t)vals[11] << 16);
-      b.z = vals[12] | ((uint32_t)vals[13] << 16); b.w = vals[14] | ((uint32_t)vals[15] << 16);
-      reinterpret_cast<uint4*>(dst)[0] = a;
-      reinterpret_cast<uint4*>(dst)[1] = b;
-    } else {
-      for (int k = 0; k < 16; ++k)
-        if (o0 + q * 16 + k < o) dst[k] = vals[k];
-    }
-  }
-}
-
 // ------------------------------------------------------------------ launchers
 hipError_t launch_quantize(const float* W, int64_t n, uint8_t* codes, uint8_t* scale8,
                            float* scale2, int32_t* flags, hipStream_t st) {
@@ -305,15 +250,6 @@ hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scale8, const flo
   else
     hipLaunchKernelGGL(k_dequant<false>, dim3((unsigned)blocks), dim3(256), 0, st, codes, scale8,
                        scale2, n, out, host_codebook());
-  return hipGetLastError();
-}
-
-hipError_t launch_dequant_t(const uint8_t* codes, const uint8_t* scale8, const float* scale2,
-                            int64_t o, int64_t d, uint16_t* WT, hipStream_t st) {
-  if (o == 0 || d == 0) return hipSuccess;
-  dim3 grid((unsigned)(d / 64), (unsigned)((o + 63) / 64));
-  hipLaunchKernelGGL(k_dequant_t, grid, dim3(256), 0, st, codes, scale8, scale2, o, d, WT,
-                     host_codebook());
   return hipGetLastError();
 }
 

@@ -59,8 +59,13 @@ def test_library_codebook_equals_oracle(L):
 
 
 def test_workspace_and_strings(L):
-    assert qb.qlora_workspace_bytes(qb.QLORA_OP_FWD, 4096, 4096, 4096, 64) > 2 * 4096 * 4096
-    assert qb.qlora_workspace_bytes(qb.QLORA_OP_BWD, 4096, 4096, 4096, 64) > 0
+    # the fused dequant-GEMM never stages a dequantized weight in the
+    # workspace: it holds only rank-r planes, independent of o·d at fixed d, o
+    for op in (qb.QLORA_OP_FWD, qb.QLORA_OP_BWD):
+        for M in (16, 2048):
+            ws = qb.qlora_workspace_bytes(op, M, 8192, 22016, 64)
+            assert 0 < ws < 2 * 8192 * 22016
+        assert qb.qlora_workspace_bytes(op, 4096, 4096, 4096, 0) == 0
     assert qb.qlora_workspace_bytes(7, 1, 64, 8, 8) == 0
     for op in (qb.QLORA_OP_FWD, qb.QLORA_OP_BWD):       # empty sizes are valid queries
         for M, d, o, r in ((0, 128, 64, 8), (8, 0, 64, 8), (8, 128, 0, 8), (0, 0, 0, 0), (1, 64, 8, 0)):
