@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--pmc", action="store_true",
+                    help="short run for hardware-counter passes: a 256 MiB device copy "
+                         "(calibration of FETCH_SIZE/WRITE_SIZE) and --steps steps, no timing")
     return ap.parse_args()
 
 
@@ -94,6 +97,18 @@ def main():
         qb.qlora_quantize_nf4_dq(W, check_finite=False, out=q)
         _, T = qb.qlora_linear_fwd(X, q, A, B, s, ws=ws_f, out=Y)
         qb.qlora_linear_bwd(dY, X, T, q, A, B, s, ws=ws_b)
+
+    if args.pmc:
+        # calibration: a plain copy of exactly 256 MiB (read 256 MiB, write 256 MiB)
+        src = torch.empty(64 << 20, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        print(json.dumps({"pmc_run": True, "copy_bytes": 256 << 20, "steps": args.steps}))
+        return
 
     for _ in range(args.warmup):
         step()

@@ -5,25 +5,29 @@
 // input gradient through Ŵᵀ; §三: dequantize the needed weights to BF16 on
 // demand, then compute base plus adapter output).
 //
-// Tile 256×256×64, 4 waves in a 2×2 grid, each wave 128×128 of fp32
-// accumulators fed by v_mfma_f32_32x32x16_bf16.  Per k-step each of the 256
-// threads owns exactly one 64-weight block of the 256×64 weight tile: it
-// loads 32 code bytes, one 8-bit scale and the group step, builds the block's
-// 16-entry table bf16(V[k]·fl32(q8·step)) (exact fp32 products, the same bits
-// as the standalone dequant), expands the 64 codes with byte permutes and
-// writes 128 bytes of bf16 into LDS.  Codes are loaded two k-steps ahead, so
-// the permute work of step s+1 overlaps the MFMAs of step s.
+// Tile 512×128×64: 4 waves stacked along M, each 128×128 of fp32
+// accumulators fed by v_mfma_f32_32x32x16_bf16.  With one wave per SIMD the
+// matrix core hides only ~100 VALU instructions per 64 MFMAs, and every
+// weight is expanded once per workgroup, so the tall tile halves the
+// expansion work per MFMA compared with 256×256.  Per k-step each of the 256
+// threads expands half of one 64-weight block: 16 code bytes, the block's
+// 8-bit scale and group step, a 16-entry table bf16(V[k]·fl32(q8·step))
+// (exact fp32 products, the same bits as the standalone dequant), byte
+// permutes, and 64 bytes of bf16 written to LDS.  Codes are loaded two
+// k-steps ahead; the activation tile goes memory -> LDS directly
+// (buffer_load ... lds), one k-step ahead.
 //
 //  * forward: the weight tile is [n][k] like the activation tile (k-major
 //    rows, XOR-swizzled 16-byte chunks), read with ds_read_b128;
 //  * backward: a block is 64 consecutive n of one k, so the tile is stored
-//    [k][n] (rows padded to 544 bytes) and the MFMA B operand is gathered
-//    with ds_read_b64_tr_b16, four k of one n per lane per read.
+//    [k][n] (16-byte chunks swizzled by 2·(k mod 4)) and the MFMA B operand
+//    is gathered with ds_read_b64_tr_b16, four k of one n per lane per read.
 // The adapter term is one (or a few) extra k-steps over [s·T ‖ B] or
 // [s·U ‖ A], accumulated into the same registers, so Y and dX are rounded
 // to bf16 once.  B [r][o] is n-major like the backward weight tile and A
-// [d][r] k-major like the forward one, so neither needs a transposed copy.  Workgroups are numbered so that each XCD (round-robin
-// dispatch over 8) works on a contiguous band of output tiles.
+// [d][r] k-major like the forward one, so neither needs a transposed copy.
+// Workgroups are numbered so that each XCD (round-robin dispatch over 8)
+// works on a contiguous band of output tiles.
 #include <type_traits>
 
 #include "kernels.h"
@@ -35,9 +39,12 @@ namespace {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int kBM = 256, kBN = 256, kBK = 64, kThreads = 256;
+constexpr int kBM = 512, kBN = 128, kBK = 64, kThreads = 256;
 
-__device__ __forceinline__ int swz8(int row) { return (row ^ (row >> 3)) & 7; }
+// XOR swizzle of the 16-byte chunks of a 128-byte LDS row: eight consecutive
+// rows, and rows 8 apart, land in different chunks.  It depends on row % 32
+// only.
+__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 3); }
 
 __device__ __forceinline__ s16x4 lds_tr(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3)))*)(p));
@@ -76,9 +83,13 @@ __device__ __forceinline__ uint4 expand(const Lut& t, uint32_t w) {
                     __builtin_amdgcn_perm(h1, l1, 0x05010400u), __builtin_amdgcn_perm(h1, l1, 0x07030602u));
 }
 
+// One block's prefetched codes and scale pieces.  ĉ = q8·step is formed only
+// when the block is expanded (a k-step later): using the loaded values at
+// load time would make the compiler wait for every load in flight.
 struct CodeReg {
-  uint4 c0, c1;
-  float chat;
+  uint4 c0;
+  uint32_t q8;
+  float step;
 };
 
 }  // namespace
@@ -110,15 +121,24 @@ __device__ __forceinline__ uint4 bload16(Rsrc r, uint32_t off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
 
+// Publish LDS written by this workgroup (ds_write and, after an explicit
+// vmcnt wait, buffer_load ... lds) without waiting for other vector-memory
+// loads still in flight: the fences cover the LDS address space only.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 template <bool kTransW>
 __global__ __launch_bounds__(kThreads) void k_qgemm(QGemmArgs p) {
-  constexpr int BSTR = kTransW ? kBN + 16 : kBK;  // bf16 per weight-tile row in LDS
-  constexpr int BROWS = kTransW ? kBK : kBN;
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][kBM * kBK];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][BROWS * BSTR];
+  // stages in separate arrays (the compiler can tell writes to the idle
+  // stage from reads of the busy one); 2 × 64 KB + 2 × 16 KB = 160 KB
+  __shared__ __attribute__((aligned(16))) uint16_t sA0[kBM * kBK], sA1[kBM * kBK];
+  __shared__ __attribute__((aligned(16))) uint16_t sB0[kBN * kBK], sB1[kBN * kBK];
 
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const int wm = w & 1, wn = w >> 1;
+  const int wq = __builtin_amdgcn_readfirstlane(w);
 
   // XCD-aware tile order: dispatch sends workgroup i to XCD i % 8; give each
   // XCD a contiguous run of tiles (row-major over the n-tiles).
@@ -128,66 +148,74 @@ __global__ __launch_bounds__(kThreads) void k_qgemm(QGemmArgs p) {
   const int per = T >> 3, rem = T & 7;
   const int v = xcd * per + min(xcd, rem) + slot;
   const int64_t m0 = (int64_t)(v / ntn) * kBM, n0 = (int64_t)(v % ntn) * kBN;
-  const int64_t mrows = min((int64_t)kBM, p.M - m0);
-
-  // activations: descriptor rebased at the tile's first row; rows past M read 0
-  const Rsrc ra_src = rsrc(p.A + m0 * p.lda, mrows * p.lda * 2);
-  const int nk = (int)((p.K + kBK - 1) / kBK);
+  const int mrows = (int)min((int64_t)kBM, p.M - m0);
   const int nk2 = (int)((p.K2 + kBK - 1) / kBK);
-  // chunk c = i*256 + t of the [256][64] tile: row c/8 = 32 i + t/8, chunk t%8
-  const uint32_t a_off0 = (uint32_t)(((t >> 3) * p.lda + (t & 7) * 8) * 2);
-  const uint32_t a_rowstep = (uint32_t)(32 * p.lda * 2);
 
-  // quantized weight: codes, 8-bit scales, steps (reads past the end give 0,
-  // which makes the block's table all zeros)
-  const int64_t nW = kTransW ? p.K * p.d : p.N * p.d;   // weights in Wq
-  const Rsrc rc = rsrc(p.codes, (nW + 7) / 8 * 4);
-  const Rsrc rs8 = rsrc(p.scale8, (nW + kBlock - 1) / kBlock);
-  const Rsrc rs2 = rsrc(p.scale2, ((nW + kBlock - 1) / kBlock + kGroup - 1) / kGroup * 4);
-  // element index of this thread's block at k-step 0, and its advance per k-step
-  const int64_t e0 = kTransW ? (int64_t)(t & 63) * p.d + n0 + 64 * (t >> 6) : (n0 + t) * p.d;
-  const int64_t e_step = kTransW ? (int64_t)kBK * p.d : kBK;
-  const bool w_row_ok = kTransW ? true : (n0 + t < p.N);
-
-  uint4 ra[8];
-  auto load_a = [&](int s) {
-    const uint32_t base = a_off0 + (uint32_t)(s * kBK * 2);
+  // ---- activation tile [512][64]: memory -> LDS (buffer_load ... lds).  Each
+  // wave instruction q fills 1 KB = 8 rows; lane l lands at byte 16·l, i.e.
+  // row 8q + l/8 of the wave's 128 and physical chunk l%8, so it fetches
+  // logical chunk (l%8) ^ swz(row).  The descriptor's base moves with k0, so
+  // a lane's offset is fixed: row·lda + 8·chunk elements, or an offset every
+  // descriptor rejects for rows past M (those read 0).  Columns are checked
+  // against klim only with kCheck (a k-step that reaches past K); without it
+  // columns past K read the next row, which is in range but must not be used.
+  const uint32_t lda2b = (uint32_t)p.lda * 2u;
+  auto dma_a = [&](auto check_tag, const uint16_t* base, uint32_t ld2b, int64_t k0, int64_t klim,
+                   uint16_t* sa) {
+    constexpr bool kCheck = decltype(check_tag)::value;
+    const int64_t left = (int64_t)mrows * (ld2b / 2) - k0;
+    const Rsrc src = rsrc(base + k0, left * 2);
+    const int krem = (int)min<int64_t>(klim - k0, kBK);   // columns of this step in range
+    // The wave's LDS rows start at sa + wrow; hiding wrow from the optimiser
+    // keeps it from holding 16 destination addresses per stage in SGPRs
+    // across the loop (each instruction then adds its constant to M0).
+    int wrow = wq * 128 * kBK;
+    asm volatile("" : "+s"(wrow));
+    uint16_t* sw = sa + wrow;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) ra[i] = bload16(ra_src, base + i * a_rowstep);
-  };
-  auto store_a = [&](uint16_t* sa) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = i * 32 + (t >> 3), ch = t & 7;
-      *reinterpret_cast<uint4*>(sa + row * kBK + ((ch ^ swz8(row)) << 3)) = ra[i];
+    for (int q = 0; q < 16; ++q) {
+      const int row = wq * 128 + q * 8 + (lane >> 3);
+      const int ch = (lane & 7) ^ swz(row);
+      uint32_t off = row < mrows ? (uint32_t)row * ld2b + (uint32_t)ch * 16u : kOobOff;
+      if (kCheck) off = ch * 8 < krem ? off : kOobOff;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          src, (__attribute__((address_space(3))) void*)(sw + q * 8 * kBK), 16, off, 0, 0, 0);
     }
   };
+  using Unchecked = std::false_type;
+  using Checked = std::true_type;
+
+  // ---- quantized weight: codes, 8-bit scales, steps.  Reads past the end
+  // give 0, which makes a block's table all zeros.  This thread's half block
+  // at k-step 0 and its advance per k-step, in weights:
+  //   forward  row n0 + t/2, k half t%2:  e0 = (n0 + t/2)·d + 32·(t%2), +64
+  //   backward row k = t%64, n half t/64: e0 = k·d + n0 + 32·(t/64),   +64·d
+  // Every offset fits in 32 bits (the host checks the weight count).
+  const uint32_t nW = (uint32_t)((kTransW ? p.K : p.N) * p.d);   // weights in Wq
+  const uint32_t nb = (nW + kBlock - 1) / kBlock;
+  const Rsrc rc = rsrc(p.codes, ((int64_t)nW + 7) / 8 * 4);
+  const Rsrc rs8 = rsrc(p.scale8, nb);
+  const Rsrc rs2 = rsrc(p.scale2, (int64_t)((nb + kGroup - 1) / kGroup) * 4);
+  const uint32_t e0 = kTransW ? (uint32_t)((t & 63) * p.d + n0 + 32 * (t >> 6))
+                              : (uint32_t)((n0 + (t >> 1)) * p.d + 32 * (t & 1));
+  const uint32_t e_step = kTransW ? (uint32_t)(kBK * p.d) : (uint32_t)kBK;
+  // rows past N (forward) or past K (backward) start at or beyond nW
+  const uint32_t c_off0 = e0 < nW ? e0 / 2 : kOobOff, b0 = e0 / kBlock;
   auto load_codes = [&](int s, CodeReg& c) {
-    const int64_t e = e0 + (int64_t)s * e_step;
-    const bool ok = w_row_ok && e < nW;
-    const uint32_t ce = ok ? (uint32_t)(e / 2) : 0x7FFFFFF0u;
-    c.c0 = bload16(rc, ce);
-    c.c1 = bload16(rc, ce + 16);
-    const uint32_t b = ok ? (uint32_t)(e / kBlock) : 0x7FFFFFF0u;
-    const uint32_t q = __builtin_amdgcn_raw_buffer_load_b8(rs8, (int)b, 0, 0);
-    const float st = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs2, (int)((b / kGroup) * 4), 0, 0));
-    c.chat = (float)q * st;
+    const uint32_t b = b0 + (uint32_t)s * (e_step / kBlock);
+    c.c0 = bload16(rc, c_off0 == kOobOff ? kOobOff : c_off0 + (uint32_t)s * (e_step / 2));
+    c.q8 = __builtin_amdgcn_raw_buffer_load_b8(rs8, (int)b, 0, 0);
+    c.step = __builtin_bit_cast(
+        float, __builtin_amdgcn_raw_buffer_load_b32(rs2, (int)(b < nb ? (b / kGroup) * 4 : kOobOff), 0, 0));
   };
-  auto dequant = [&](const CodeReg& c, uint4 (&o)[8]) {
-    Lut lut;
-    make_lut(p.cb, c.chat, lut);
-    const uint32_t ws[8] = {c.c0.x, c.c0.y, c.c0.z, c.c0.w, c.c1.x, c.c1.y, c.c1.z, c.c1.w};
-#pragma unroll
-    for (int j = 0; j < 8; ++j) o[j] = expand(lut, ws[j]);
-  };
-  auto store_w = [&](const uint4 (&o)[8], uint16_t* sb) {
+  // LDS position of 16-byte chunk `ch` (0..3) of this thread's half block
+  auto w_slot = [&](uint16_t* sb, int ch) -> uint16_t* {
     if (!kTransW) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) *reinterpret_cast<uint4*>(sb + t * kBK + ((j ^ swz8(t)) << 3)) = o[j];
+      const int row = t >> 1;
+      return sb + row * kBK + (((4 * (t & 1) + ch) ^ swz(row)) << 3);
     } else {
-      uint16_t* row = sb + (t & 63) * BSTR + 64 * (t >> 6);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) *reinterpret_cast<uint4*>(row + 8 * j) = o[j];
+      const int k = t & 63;
+      return sb + k * kBN + (((4 * (t >> 6) + ch) ^ ((k & 3) << 1)) << 3);
     }
   };
 
@@ -199,136 +227,188 @@ __global__ __launch_bounds__(kThreads) void k_qgemm(QGemmArgs p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
+  // Fragments of one 16-wide k sub-step: 4 activation row blocks × 4 weight
+  // column blocks.  kBTr: the weight-side tile is [k][n] (read transposed).
+  // swz(row) depends on row % 32 only, so the four row blocks of a fragment
+  // set differ by constant offsets.
+  struct Frags {
+    bf16x8 a[4], b[4];
+  };
+  auto read_frags = [&](auto btr_tag, Frags& f, const uint16_t* sa, const uint16_t* sb, int kk) {
+    constexpr bool kBTr = decltype(btr_tag)::value;
+    const int ch = kk * 2 + (lane >> 5);
+    const int r32 = lane & 31;
+    const uint16_t* pa = sa + (wq * 128 + r32) * kBK + ((ch ^ swz(r32)) << 3);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f.a[i] = *reinterpret_cast<const bf16x8*>(pa + i * 32 * kBK);
+    if (!kBTr) {
+      const uint16_t* pb = sb + r32 * kBK + ((ch ^ swz(r32)) << 3);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) f.b[j] = *reinterpret_cast<const bf16x8*>(pb + j * 32 * kBK);
+    } else {
+      const int g = lane >> 4, s = lane & 15;
+      const int kr = kk * 16 + 8 * (g >> 1) + (s >> 2);          // kr % 4 == s / 4
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = j * 4 + 2 * (g & 1) + ((s & 3) >> 1);        // logical 16-byte chunk
+        const uint16_t* q = sb + kr * kBN + ((c ^ ((kr & 3) << 1)) << 3) + 4 * (s & 1);
+        const s16x4 lo = lds_tr(q);
+        const s16x4 hi = lds_tr(q + 4 * kBN);                       // rows kr+4: same swizzle
+        const s16x8 bv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        f.b[j] = __builtin_bit_cast(bf16x8, bv);
+      }
+    }
+  };
   // The weight fragment is the MFMA's first operand and the activation
   // fragment its second, so each lane accumulates 4 consecutive output
   // columns of one output row (the epilogue stores 8 bytes at a time).
-  // kBTr: the weight-side tile is [k][n] (read transposed) instead of [n][k].
-  auto compute = [&](auto btr_tag, const uint16_t* sa, const uint16_t* sb) {
-    constexpr bool kBTr = decltype(btr_tag)::value;
-    constexpr int TSTR = kBN + 16;
+  auto mfma16 = [&](const Frags& f) {
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      bf16x8 a[4], b[4];
-      const int ch = kk * 2 + (lane >> 5);
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = wm * 128 + i * 32 + (lane & 31);
-        a[i] = *reinterpret_cast<const bf16x8*>(sa + row * kBK + ((ch ^ swz8(row)) << 3));
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (!kBTr) {
-          const int row = wn * 128 + j * 32 + (lane & 31);
-          b[j] = *reinterpret_cast<const bf16x8*>(sb + row * kBK + ((ch ^ swz8(row)) << 3));
-        } else {
-          const int g = lane >> 4, s = lane & 15;
-          const int col = wn * 128 + j * 32 + 16 * (g & 1) + 4 * (s & 3);
-          const int kr = kk * 16 + 8 * (g >> 1) + (s >> 2);
-          const s16x4 lo = lds_tr(sb + kr * TSTR + col);
-          const s16x4 hi = lds_tr(sb + (kr + 4) * TSTR + col);
-          const s16x8 bv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          b[j] = __builtin_bit_cast(bf16x8, bv);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
-    }
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
   };
   using WTag = std::integral_constant<bool, kTransW>;
   using ATag = std::integral_constant<bool, !kTransW>;
+  const uint16_t* a_base = p.A + m0 * p.lda;
 
-  // ---- main loop over the quantized weight: one branch-free block per k-step
-  if (nk > 0) {
-    CodeReg r0, r1;
-    load_codes(0, r0);
-    load_codes(1, r1);
-    load_a(0);
-    {
-      uint4 dq[8];
-      dequant(r0, dq);
-      store_a(sA[0]);
-      store_w(dq, sB[0]);
+  // One k-step without pipelining (the partial last weight step and the
+  // adapter steps): publish the staged tiles, 16 MFMAs per sub-step, and
+  // release the buffers.
+  auto plain_step = [&](auto btr_tag) {
+    __builtin_amdgcn_s_waitcnt((0 & 0xF) | (0x7 << 4) | (0xF << 8));
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      Frags f;
+      read_frags(btr_tag, f, sA0, sB0, kk);
+      mfma16(f);
     }
     __syncthreads();
-    // step s: prefetch activations of s+1 and codes of s+2, expand the codes
-    // of s+1, multiply step s, then publish s+1 (past the end the extra
-    // loads read zeros or in-range data and land in the idle buffer)
-    auto iteration = [&](int s, CodeReg& refill, const CodeReg& next) {
-      const int cur = s & 1;
-      load_a(s + 1);
+  };
+  auto expand_block = [&](const CodeReg& c, uint16_t* sb) {
+    Lut lut;
+    make_lut(p.cb, (float)c.q8 * c.step, lut);   // ĉ = fl32(q8·step)
+    const uint32_t ws[4] = {c.c0.x, c.c0.y, c.c0.z, c.c0.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) *reinterpret_cast<uint4*>(w_slot(sb, k)) = expand(lut, ws[k]);
+  };
+
+  // ---- main loop over the full k-steps of the quantized weight: one
+  // branch-free half block per thread per k-step.  vmcnt(N) waits until at
+  // most N vector-memory operations are in flight: the 3 code/scale loads of
+  // step s+2 are issued after the activation DMA of step s+1, so vmcnt(3)
+  // waits for the DMA only.
+  const int nkf = (int)(p.K / kBK);
+  constexpr int kWaitDma = (3 & 0xF) | (0x7 << 4) | (0xF << 8);
+  if (nkf > 0) {
+    CodeReg r0, r1;
+    dma_a(Unchecked{}, a_base, lda2b, 0, p.K, sA0);
+    load_codes(0, r0);
+    load_codes(1, r1);
+    expand_block(r0, sB0);
+    __builtin_amdgcn_s_waitcnt(kWaitDma);
+    __syncthreads();
+    // step s: DMA the activations of s+1, load the codes of s+2, and per
+    // 16-wide k sub-step read fragments, expand one code word of s+1 into the
+    // idle weight buffer, and issue 16 MFMAs; then wait for the DMA and
+    // publish.  Loads for steps at or past nkf land in the idle buffers and
+    // are never used.
+    auto iteration = [&](auto stage, int s, CodeReg& refill, const CodeReg& next) {
+      constexpr bool kOdd = decltype(stage)::value;
+      uint16_t* a_cur = kOdd ? sA1 : sA0;
+      uint16_t* a_nxt = kOdd ? sA0 : sA1;
+      uint16_t* b_cur = kOdd ? sB1 : sB0;
+      uint16_t* b_nxt = kOdd ? sB0 : sB1;
+      // issue order: fragments of sub-step 0, the DMA, then the code loads
+      // (the vmcnt wait at the end relies on the code loads being last)
+      Frags f[2];
+      read_frags(WTag{}, f[0], a_cur, b_cur, 0);
+      dma_a(Unchecked{}, a_base, lda2b, (int64_t)(s + 1) * kBK, p.K, a_nxt);
+      __builtin_amdgcn_sched_barrier(0);
       load_codes(s + 2, refill);
-      uint4 dq[8];
-      dequant(next, dq);
-      compute(WTag{}, sA[cur], sB[cur]);
-      store_a(sA[cur ^ 1]);
-      store_w(dq, sB[cur ^ 1]);
-      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+      Lut lut;
+      make_lut(p.cb, (float)next.q8 * next.step, lut);   // ĉ = fl32(q8·step)
+      const uint32_t ws[4] = {next.c0.x, next.c0.y, next.c0.z, next.c0.w};
+      // fragments of sub-step kk+1 are read while the MFMAs of kk run
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        if (kk < 3) read_frags(WTag{}, f[(kk + 1) & 1], a_cur, b_cur, kk + 1);
+        *reinterpret_cast<uint4*>(w_slot(b_nxt, kk)) = expand(lut, ws[kk]);
+        mfma16(f[kk & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      __builtin_amdgcn_s_waitcnt(kWaitDma);
+      lds_barrier();
     };
     int s = 0;
-    for (; s + 1 < nk; s += 2) {
-      iteration(s, r0, r1);
-      iteration(s + 1, r1, r0);
+    for (; s + 1 < nkf; s += 2) {
+      iteration(std::false_type{}, s, r0, r1);
+      iteration(std::true_type{}, s + 1, r1, r0);
     }
-    if (s < nk) iteration(s, r0, r1);
+    if (s < nkf) iteration(std::false_type{}, s, r0, r1);
+  }
+  // ---- the partial last k-step (K % 64 != 0): weight rows past K read 0
+  if (nkf * kBK < p.K) {
+    CodeReg c;
+    dma_a(Checked{}, a_base, lda2b, (int64_t)nkf * kBK, p.K, sA0);
+    load_codes(nkf, c);
+    expand_block(c, sB0);
+    plain_step(WTag{});
   }
 
-  // ---- adapter k-steps: [s·T ‖ B] (forward, B is [r][N]: an n-major tile
-  // read transposed) or [s·U ‖ A] (backward, A is [N][r]: a k-major tile)
+  // ---- adapter k-steps: [s·T ‖ B] (forward: B [r][N] is an n-major tile,
+  // read transposed) or [s·U ‖ A] (backward: A [N][r] is a k-major tile)
   if (nk2 > 0) {
-    constexpr int TSTR = kBN + 16;
-    uint16_t* sb = &sB[0][0];          // spans both stages (up to 34 KB used)
-    const Rsrc r2 = rsrc(p.A2 + m0 * p.lda2, mrows * p.lda2 * 2);
+    const uint16_t* a2_base = p.A2 + m0 * p.lda2;
     const Rsrc rb2 = !kTransW ? rsrc(p.B2, p.K2 * p.ldb2 * 2)
                               : rsrc(p.B2 + n0 * p.ldb2, min((int64_t)kBN, p.N - n0) * p.ldb2 * 2);
     for (int ls = 0; ls < nk2; ++ls) {
       const int64_t k0 = (int64_t)ls * kBK;
-      uint4 rb[8];
+      dma_a(Checked{}, a2_base, (uint32_t)p.lda2 * 2u, k0, p.K2, sA0);
+      uint4 rb[4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int c = i * kThreads + t;
-        const int row = c >> 3;
-        const int64_t gk = k0 + (c & 7) * 8;
-        ra[i] = bload16(r2, gk < p.K2 ? (uint32_t)((row * p.lda2 + gk) * 2) : kOobOff);
-        if (kTransW) {   // A rows n, k-major
+      for (int i = 0; i < 4; ++i) {
+        const int c = i * kThreads + t;        // 1024 chunks of 16 bytes
+        if (kTransW) {   // A rows n (128) × 8 chunks of k
+          const int row = c >> 3, ch = c & 7;
+          const int64_t gk = k0 + ch * 8;
           rb[i] = bload16(rb2, gk < p.K2 ? (uint32_t)((row * p.ldb2 + gk) * 2) : kOobOff);
-        } else {         // B rows k, n-major
-          const int kr = c >> 5;
-          const int64_t gk2 = k0 + kr, gn = n0 + (c & 31) * 8;
-          rb[i] = bload16(rb2, (gk2 < p.K2 && gn < p.N) ? (uint32_t)((gk2 * p.ldb2 + gn) * 2) : kOobOff);
+        } else {         // B rows k (64) × 16 chunks of n
+          const int kr = c >> 4, ch = c & 15;
+          const int64_t gk = k0 + kr, gn = n0 + ch * 8;
+          rb[i] = bload16(rb2, (gk < p.K2 && gn < p.N) ? (uint32_t)((gk * p.ldb2 + gn) * 2) : kOobOff);
         }
       }
-      store_a(sA[0]);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < 4; ++i) {
         const int c = i * kThreads + t;
         if (kTransW) {
           const int row = c >> 3, ch = c & 7;
-          *reinterpret_cast<uint4*>(sb + row * kBK + ((ch ^ swz8(row)) << 3)) = rb[i];
+          *reinterpret_cast<uint4*>(sB0 + row * kBK + ((ch ^ swz(row)) << 3)) = rb[i];
         } else {
-          *reinterpret_cast<uint4*>(sb + (c >> 5) * TSTR + (c & 31) * 8) = rb[i];
+          const int kr = c >> 4, ch = c & 15;
+          *reinterpret_cast<uint4*>(sB0 + kr * kBN + ((ch ^ ((kr & 3) << 1)) << 3)) = rb[i];
         }
       }
-      __syncthreads();
-      compute(ATag{}, sA[0], sb);
-      __syncthreads();
+      plain_step(ATag{});
     }
   }
 
   // ---- epilogue: lane holds output row m = lane%32 of each 32×32 block and
   // columns 8(e/4) + 4(lane/32) + e%4: four consecutive columns per 8-byte store
-  const Rsrc rcout = rsrc(p.C + m0 * p.ldc, mrows * p.ldc * 2);
+  const Rsrc rcout = rsrc(p.C + m0 * p.ldc, (int64_t)mrows * p.ldc * 2);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int row = wm * 128 + i * 32 + (lane & 31);
-        const int64_t col = n0 + wn * 128 + j * 32 + q * 8 + (lane >> 5) * 4;
-        const uint32_t off = col < p.N ? (uint32_t)((row * p.ldc + col) * 2) : 0x7FFFFFF0u;
+        const int row = wq * 128 + i * 32 + (lane & 31);
+        const int64_t col = n0 + j * 32 + q * 8 + (lane >> 5) * 4;
+        const uint32_t off = col < p.N ? (uint32_t)((row * p.ldc + col) * 2) : kOobOff;
         const uint32_t lo = pack_bf16x2(acc[i][j][4 * q + 0], acc[i][j][4 * q + 1]);
         const uint32_t hi = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
         typedef int i32x2 __attribute__((ext_vector_type(2)));
