@@ -153,7 +153,7 @@ def main():
             pmc = json.load(f)
         if pmc.get("kernel_source_hash") == kernel_source_hash() and pmc.get("workload") == wl.name:
             traffic = pmc.get("hbm_bytes_per_launch")
-    roofline = {"bound": "mfma", "kernel": "k_qgemm fused NF4 dequant-GEMM 256x256 (Y = X·Ŵ + sT·B, dX = dY·Ŵᵀ + sU·Aᵀ)",
+    roofline = {"bound": "mfma", "kernel": "k_qgemm fused NF4 dequant-GEMM 512x128 (Y = X·Ŵ + sT·B, dX = dY·Ŵᵀ + sU·Aᵀ)",
                 "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                 "flop_per_launch": gemm_flop_per_launch, "avg_launch_us": round(gemm_avg_ms * 1e3, 2),

@@ -6,21 +6,21 @@
 // demand, then compute base plus adapter output).
 //
 // Tile 512×128×64: 4 waves stacked along M, each 128×128 of fp32
-// accumulators fed by v_mfma_f32_32x32x16_bf16.  With one wave per SIMD the
-// matrix core hides only ~100 VALU instructions per 64 MFMAs, and every
-// weight is expanded once per workgroup, so the tall tile halves the
-// expansion work per MFMA compared with 256×256.  Per k-step each of the 256
-// threads expands half of one 64-weight block: 16 code bytes, the block's
-// 8-bit scale and group step, a 16-entry table bf16(V[k]·fl32(q8·step))
-// (exact fp32 products, the same bits as the standalone dequant), byte
-// permutes, and 64 bytes of bf16 written to LDS.  Codes are loaded two
-// k-steps ahead; the activation tile goes memory -> LDS directly
-// (buffer_load ... lds), one k-step ahead.
+// accumulators fed by v_mfma_f32_32x32x16_bf16.  Every weight is expanded
+// once per workgroup, so the tall tile halves the expansion work per MFMA
+// compared with 256×256.  Per k-step each of the 256 threads expands half of
+// one 64-weight block: 16 code bytes, the block's 8-bit scale and group
+// step, a 16-entry table bf16(V[k]·fl32(q8·step)) (exact fp32 products, the
+// same bits as the standalone dequant), byte permutes, and 64 bytes of bf16
+// written to LDS.  The activation tile goes memory -> LDS directly
+// (buffer_load ... lds) one k-step ahead, its instructions spread between
+// the MFMAs; each wave loads exactly the 128 rows it multiplies.  Codes are
+// loaded one k-step ahead of their expansion.
 //
 //  * forward: the weight tile is [n][k] like the activation tile (k-major
 //    rows, XOR-swizzled 16-byte chunks), read with ds_read_b128;
 //  * backward: a block is 64 consecutive n of one k, so the tile is stored
-//    [k][n] (16-byte chunks swizzled by 2·(k mod 4)) and the MFMA B operand
+//    [k][n] (16-byte chunks swizzled by 4·(k mod 4)) and the MFMA B operand
 //    is gathered with ds_read_b64_tr_b16, four k of one n per lane per read.
 // The adapter term is one (or a few) extra k-steps over [s·T ‖ B] or
 // [s·U ‖ A], accumulated into the same registers, so Y and dX are rounded
@@ -39,7 +39,11 @@ namespace {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int kBM = 512, kBN = 128, kBK = 64, kThreads = 256;
+constexpr int kBM = 512, kBN = 128, kBK = 64;
+// Waves per workgroup: 4 (one per SIMD, 128 rows each, accumulators in
+// AGPRs) or 8 (two per SIMD, 64 rows each).  Both measure the same on the
+// 4096-square layer; 4 keeps the register budget simple.
+constexpr int kWaves = 4;
 
 // XOR swizzle of the 16-byte chunks of a 128-byte LDS row: eight consecutive
 // rows, and rows 8 apart, land in different chunks.  It depends on row % 32
@@ -83,14 +87,6 @@ __device__ __forceinline__ uint4 expand(const Lut& t, uint32_t w) {
                     __builtin_amdgcn_perm(h1, l1, 0x05010400u), __builtin_amdgcn_perm(h1, l1, 0x07030602u));
 }
 
-// One block's prefetched codes and scale pieces.  ĉ = q8·step is formed only
-// when the block is expanded (a k-step later): using the loaded values at
-// load time would make the compiler wait for every load in flight.
-struct CodeReg {
-  uint4 c0;
-  uint32_t q8;
-  float step;
-};
 
 }  // namespace
 
@@ -130,8 +126,17 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-template <bool kTransW>
-__global__ __launch_bounds__(kThreads) void k_qgemm(QGemmArgs p) {
+template <bool kTransW, int kWaves>
+__global__ __launch_bounds__(64 * kWaves) void k_qgemm(QGemmArgs p) {
+  constexpr int kT = 64 * kWaves;        // threads
+  constexpr int kWR = kBM / kWaves;      // activation rows per wave
+  constexpr int kI = kWR / 32;           // 32-row MFMA blocks per wave
+  constexpr int kQ = kWR / 8;            // DMA instructions per wave per k-step
+  constexpr int kWT = kBN * kBK / kT;    // weights one thread expands per k-step
+  constexpr int kCW = kWT / 8;           // code words (8 codes each) per thread
+  constexpr int kParts = kBlock / kWT;   // threads sharing one 64-weight block
+  static_assert(kCW == 2 || kCW == 4, "a thread expands 16 or 32 weights");
+
   // stages in separate arrays (the compiler can tell writes to the idle
   // stage from reads of the busy one); 2 × 64 KB + 2 × 16 KB = 160 KB
   __shared__ __attribute__((aligned(16))) uint16_t sA0[kBM * kBK], sA1[kBM * kBK];
@@ -153,7 +158,7 @@ __global__ __launch_bounds__(kThreads) void k_qgemm(QGemmArgs p) {
 
   // ---- activation tile [512][64]: memory -> LDS (buffer_load ... lds).  Each
   // wave instruction q fills 1 KB = 8 rows; lane l lands at byte 16·l, i.e.
-  // row 8q + l/8 of the wave's 128 and physical chunk l%8, so it fetches
+  // row 8q + l/8 of the wave's rows and physical chunk l%8, so it fetches
   // logical chunk (l%8) ^ swz(row).  The descriptor's base moves with k0, so
   // a lane's offset is fixed: row·lda + 8·chunk elements, or an offset every
   // descriptor rejects for rows past M (those read 0).  Columns are checked
@@ -161,20 +166,21 @@ __global__ __launch_bounds__(kThreads) void k_qgemm(QGemmArgs p) {
   // columns past K read the next row, which is in range but must not be used.
   const uint32_t lda2b = (uint32_t)p.lda * 2u;
   auto dma_a = [&](auto check_tag, const uint16_t* base, uint32_t ld2b, int64_t k0, int64_t klim,
-                   uint16_t* sa) {
+                   uint16_t* sa, int qlo = 0, int qhi = kBM / 8) {
     constexpr bool kCheck = decltype(check_tag)::value;
     const int64_t left = (int64_t)mrows * (ld2b / 2) - k0;
     const Rsrc src = rsrc(base + k0, left * 2);
     const int krem = (int)min<int64_t>(klim - k0, kBK);   // columns of this step in range
     // The wave's LDS rows start at sa + wrow; hiding wrow from the optimiser
-    // keeps it from holding 16 destination addresses per stage in SGPRs
-    // across the loop (each instruction then adds its constant to M0).
-    int wrow = wq * 128 * kBK;
+    // keeps it from holding every destination address of both stages in
+    // SGPRs across the loop (each instruction then adds its constant to M0).
+    int wrow = wq * kWR * kBK;
     asm volatile("" : "+s"(wrow));
     uint16_t* sw = sa + wrow;
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int row = wq * 128 + q * 8 + (lane >> 3);
+    for (int q = 0; q < kQ; ++q) {
+      if (q < qlo || q >= qhi) continue;
+      const int row = wq * kWR + q * 8 + (lane >> 3);
       const int ch = (lane & 7) ^ swz(row);
       uint32_t off = row < mrows ? (uint32_t)row * ld2b + (uint32_t)ch * 16u : kOobOff;
       if (kCheck) off = ch * 8 < krem ? off : kOobOff;
@@ -186,61 +192,77 @@ __global__ __launch_bounds__(kThreads) void k_qgemm(QGemmArgs p) {
   using Checked = std::true_type;
 
   // ---- quantized weight: codes, 8-bit scales, steps.  Reads past the end
-  // give 0, which makes a block's table all zeros.  This thread's half block
-  // at k-step 0 and its advance per k-step, in weights:
-  //   forward  row n0 + t/2, k half t%2:  e0 = (n0 + t/2)·d + 32·(t%2), +64
-  //   backward row k = t%64, n half t/64: e0 = k·d + n0 + 32·(t/64),   +64·d
+  // give 0, which makes a block's table all zeros.  kParts consecutive
+  // threads share a block; thread part pp expands weights kWT·pp .. +kWT-1
+  // of it.  At k-step 0, in weights (advance per k-step):
+  //   forward  row n = t / kParts:              e0 = (n0 + n)·d + kWT·pp        (+64)
+  //   backward row k = (t / kParts) % 64, block hb = t / (64·kParts) of the
+  //            tile's two: e0 = k·d + n0 + 64·hb + kWT·pp                    (+64·d)
   // Every offset fits in 32 bits (the host checks the weight count).
+  const int pp = t % kParts;
+  const int wrow_n = t / kParts;                     // forward: tile row n
+  const int wrow_k = (t / kParts) & 63, hb = t / (64 * kParts);   // backward
   const uint32_t nW = (uint32_t)((kTransW ? p.K : p.N) * p.d);   // weights in Wq
   const uint32_t nb = (nW + kBlock - 1) / kBlock;
   const Rsrc rc = rsrc(p.codes, ((int64_t)nW + 7) / 8 * 4);
   const Rsrc rs8 = rsrc(p.scale8, nb);
   const Rsrc rs2 = rsrc(p.scale2, (int64_t)((nb + kGroup - 1) / kGroup) * 4);
-  const uint32_t e0 = kTransW ? (uint32_t)((t & 63) * p.d + n0 + 32 * (t >> 6))
-                              : (uint32_t)((n0 + (t >> 1)) * p.d + 32 * (t & 1));
+  const uint32_t e0 = kTransW ? (uint32_t)(wrow_k * p.d + n0 + 64 * hb + kWT * pp)
+                              : (uint32_t)((n0 + wrow_n) * p.d + kWT * pp);
   const uint32_t e_step = kTransW ? (uint32_t)(kBK * p.d) : (uint32_t)kBK;
   // rows past N (forward) or past K (backward) start at or beyond nW
   const uint32_t c_off0 = e0 < nW ? e0 / 2 : kOobOff, b0 = e0 / kBlock;
-  auto load_codes = [&](int s, CodeReg& c) {
+  struct Codes {
+    uint32_t c[kCW];
+    uint32_t q8;
+    float step;
+  };
+  auto load_codes = [&](int s, Codes& c) {
     const uint32_t b = b0 + (uint32_t)s * (e_step / kBlock);
-    c.c0 = bload16(rc, c_off0 == kOobOff ? kOobOff : c_off0 + (uint32_t)s * (e_step / 2));
+    const uint32_t o = c_off0 == kOobOff ? kOobOff : c_off0 + (uint32_t)s * (e_step / 2);
+    if constexpr (kCW == 4) {
+      const uint4 x = bload16(rc, o);
+      c.c[0] = x.x; c.c[1] = x.y; c.c[2] = x.z; c.c[3] = x.w;
+    } else {
+      typedef int i32x2 __attribute__((ext_vector_type(2)));
+      const i32x2 x = __builtin_amdgcn_raw_buffer_load_b64(rc, (int)o, 0, 0);
+      c.c[0] = (uint32_t)x[0]; c.c[1] = (uint32_t)x[1];
+    }
     c.q8 = __builtin_amdgcn_raw_buffer_load_b8(rs8, (int)b, 0, 0);
     c.step = __builtin_bit_cast(
         float, __builtin_amdgcn_raw_buffer_load_b32(rs2, (int)(b < nb ? (b / kGroup) * 4 : kOobOff), 0, 0));
   };
-  // LDS position of 16-byte chunk `ch` (0..3) of this thread's half block
-  auto w_slot = [&](uint16_t* sb, int ch) -> uint16_t* {
+  // LDS position of code word c's 8 weights (one 16-byte chunk)
+  auto w_slot = [&](uint16_t* sb, int c) -> uint16_t* {
     if (!kTransW) {
-      const int row = t >> 1;
-      return sb + row * kBK + (((4 * (t & 1) + ch) ^ swz(row)) << 3);
+      return sb + wrow_n * kBK + (((kCW * pp + c) ^ swz(wrow_n)) << 3);
     } else {
-      const int k = t & 63;
-      return sb + k * kBN + (((4 * (t >> 6) + ch) ^ ((k & 3) << 1)) << 3);
+      return sb + wrow_k * kBN + (((8 * hb + kCW * pp + c) ^ ((wrow_k & 3) << 2)) << 3);
     }
   };
 
-  f32x16 acc[4][4];
+  f32x16 acc[kI][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kI; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  // Fragments of one 16-wide k sub-step: 4 activation row blocks × 4 weight
+  // Fragments of one 16-wide k sub-step: kI activation row blocks × 4 weight
   // column blocks.  kBTr: the weight-side tile is [k][n] (read transposed).
-  // swz(row) depends on row % 32 only, so the four row blocks of a fragment
-  // set differ by constant offsets.
+  // swz(row) depends on row % 32 only, so the row blocks of a fragment set
+  // differ by constant offsets.
   struct Frags {
-    bf16x8 a[4], b[4];
+    bf16x8 a[kI], b[4];
   };
   auto read_frags = [&](auto btr_tag, Frags& f, const uint16_t* sa, const uint16_t* sb, int kk) {
     constexpr bool kBTr = decltype(btr_tag)::value;
     const int ch = kk * 2 + (lane >> 5);
     const int r32 = lane & 31;
-    const uint16_t* pa = sa + (wq * 128 + r32) * kBK + ((ch ^ swz(r32)) << 3);
+    const uint16_t* pa = sa + (wq * kWR + r32) * kBK + ((ch ^ swz(r32)) << 3);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) f.a[i] = *reinterpret_cast<const bf16x8*>(pa + i * 32 * kBK);
+    for (int i = 0; i < kI; ++i) f.a[i] = *reinterpret_cast<const bf16x8*>(pa + i * 32 * kBK);
     if (!kBTr) {
       const uint16_t* pb = sb + r32 * kBK + ((ch ^ swz(r32)) << 3);
 #pragma unroll
@@ -250,8 +272,9 @@ __global__ __launch_bounds__(kThreads) void k_qgemm(QGemmArgs p) {
       const int kr = kk * 16 + 8 * (g >> 1) + (s >> 2);          // kr % 4 == s / 4
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int c = j * 4 + 2 * (g & 1) + ((s & 3) >> 1);        // logical 16-byte chunk
-        const uint16_t* q = sb + kr * kBN + ((c ^ ((kr & 3) << 1)) << 3) + 4 * (s & 1);
+        // logical 16-byte chunk 4j + 2(g%2) + (s%4)/2, swizzled by 4·(kr%4)
+        const int c = 4 * (j ^ (s >> 2)) + 2 * (g & 1) + ((s & 3) >> 1);
+        const uint16_t* q = sb + kr * kBN + (c << 3) + 4 * (s & 1);
         const s16x4 lo = lds_tr(q);
         const s16x4 hi = lds_tr(q + 4 * kBN);                       // rows kr+4: same swizzle
         const s16x8 bv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -262,9 +285,9 @@ __global__ __launch_bounds__(kThreads) void k_qgemm(QGemmArgs p) {
   // The weight fragment is the MFMA's first operand and the activation
   // fragment its second, so each lane accumulates 4 consecutive output
   // columns of one output row (the epilogue stores 8 bytes at a time).
-  auto mfma16 = [&](const Frags& f) {
+  auto mfmas = [&](const Frags& f) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kI; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
@@ -274,7 +297,7 @@ __global__ __launch_bounds__(kThreads) void k_qgemm(QGemmArgs p) {
   const uint16_t* a_base = p.A + m0 * p.lda;
 
   // One k-step without pipelining (the partial last weight step and the
-  // adapter steps): publish the staged tiles, 16 MFMAs per sub-step, and
+  // adapter steps): publish the staged tiles, MFMAs per sub-step, and
   // release the buffers.
   auto plain_step = [&](auto btr_tag) {
     __builtin_amdgcn_s_waitcnt((0 & 0xF) | (0x7 << 4) | (0xF << 8));
@@ -283,64 +306,64 @@ __global__ __launch_bounds__(kThreads) void k_qgemm(QGemmArgs p) {
     for (int kk = 0; kk < 4; ++kk) {
       Frags f;
       read_frags(btr_tag, f, sA0, sB0, kk);
-      mfma16(f);
+      mfmas(f);
     }
     __syncthreads();
   };
-  auto expand_block = [&](const CodeReg& c, uint16_t* sb) {
+  auto expand_block = [&](const Codes& c, uint16_t* sb) {
     Lut lut;
     make_lut(p.cb, (float)c.q8 * c.step, lut);   // ĉ = fl32(q8·step)
-    const uint32_t ws[4] = {c.c0.x, c.c0.y, c.c0.z, c.c0.w};
 #pragma unroll
-    for (int k = 0; k < 4; ++k) *reinterpret_cast<uint4*>(w_slot(sb, k)) = expand(lut, ws[k]);
+    for (int k = 0; k < kCW; ++k) *reinterpret_cast<uint4*>(w_slot(sb, k)) = expand(lut, c.c[k]);
   };
 
-  // ---- main loop over the full k-steps of the quantized weight: one
-  // branch-free half block per thread per k-step.  vmcnt(N) waits until at
-  // most N vector-memory operations are in flight: the 3 code/scale loads of
-  // step s+2 are issued after the activation DMA of step s+1, so vmcnt(3)
-  // waits for the DMA only.
+  // ---- main loop over the full k-steps of the quantized weight
   const int nkf = (int)(p.K / kBK);
-  constexpr int kWaitDma = (3 & 0xF) | (0x7 << 4) | (0xF << 8);
+  constexpr int kWaitAll = (0 & 0xF) | (0x7 << 4) | (0xF << 8);   // vmcnt(0)
   if (nkf > 0) {
-    CodeReg r0, r1;
+    Codes r0, r1;
     dma_a(Unchecked{}, a_base, lda2b, 0, p.K, sA0);
     load_codes(0, r0);
     load_codes(1, r1);
     expand_block(r0, sB0);
-    __builtin_amdgcn_s_waitcnt(kWaitDma);
+    __builtin_amdgcn_s_waitcnt(kWaitAll);
     __syncthreads();
-    // step s: DMA the activations of s+1, load the codes of s+2, and per
-    // 16-wide k sub-step read fragments, expand one code word of s+1 into the
-    // idle weight buffer, and issue 16 MFMAs; then wait for the DMA and
-    // publish.  Loads for steps at or past nkf land in the idle buffers and
-    // are never used.
-    auto iteration = [&](auto stage, int s, CodeReg& refill, const CodeReg& next) {
+    // step s: per 16-wide k sub-step read the fragments of the next
+    // sub-step, issue a share of the activation DMA of s+1 (the code loads of
+    // s+2 go out with the second share and get most of a step), expand code words
+    // of s+1 into the idle weight buffer and issue the MFMAs, DMA instructions
+    // interleaved with MFMAs so the address FIFO never backs up and stalls the
+    // wave; then wait for the DMA and publish.  Loads for steps at or past nkf
+    // land in the idle buffers and are never used.
+    auto iteration = [&](auto stage, int s, Codes& refill, const Codes& next) {
       constexpr bool kOdd = decltype(stage)::value;
       uint16_t* a_cur = kOdd ? sA1 : sA0;
       uint16_t* a_nxt = kOdd ? sA0 : sA1;
       uint16_t* b_cur = kOdd ? sB1 : sB0;
       uint16_t* b_nxt = kOdd ? sB0 : sB1;
-      // issue order: fragments of sub-step 0, the DMA, then the code loads
-      // (the vmcnt wait at the end relies on the code loads being last)
       Frags f[2];
       read_frags(WTag{}, f[0], a_cur, b_cur, 0);
-      dma_a(Unchecked{}, a_base, lda2b, (int64_t)(s + 1) * kBK, p.K, a_nxt);
-      __builtin_amdgcn_sched_barrier(0);
-      load_codes(s + 2, refill);
       __builtin_amdgcn_sched_barrier(0);
       Lut lut;
       make_lut(p.cb, (float)next.q8 * next.step, lut);   // ĉ = fl32(q8·step)
-      const uint32_t ws[4] = {next.c0.x, next.c0.y, next.c0.z, next.c0.w};
-      // fragments of sub-step kk+1 are read while the MFMAs of kk run
+      constexpr int kPer = kQ / 4;          // DMA instructions per sub-step
+      constexpr int kMfma = 4 * kI;         // MFMAs per sub-step
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         if (kk < 3) read_frags(WTag{}, f[(kk + 1) & 1], a_cur, b_cur, kk + 1);
-        *reinterpret_cast<uint4*>(w_slot(b_nxt, kk)) = expand(lut, ws[kk]);
-        mfma16(f[kk & 1]);
+        if (kk == 1) load_codes(s + 2, refill);
+        dma_a(Unchecked{}, a_base, lda2b, (int64_t)(s + 1) * kBK, p.K, a_nxt, kk * kPer, kk * kPer + kPer);
+        if (kk % (4 / kCW) == 0)
+          *reinterpret_cast<uint4*>(w_slot(b_nxt, kk / (4 / kCW))) = expand(lut, next.c[kk / (4 / kCW)]);
+        mfmas(f[kk & 1]);
+#pragma unroll
+        for (int x = 0; x < kPer; ++x) {
+          __builtin_amdgcn_sched_group_barrier(0x008, kMfma / kPer / 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_s_waitcnt(kWaitDma);
+      __builtin_amdgcn_s_waitcnt(kWaitAll);
       lds_barrier();
     };
     int s = 0;
@@ -352,7 +375,7 @@ __global__ __launch_bounds__(kThreads) void k_qgemm(QGemmArgs p) {
   }
   // ---- the partial last k-step (K % 64 != 0): weight rows past K read 0
   if (nkf * kBK < p.K) {
-    CodeReg c;
+    Codes c;
     dma_a(Checked{}, a_base, lda2b, (int64_t)nkf * kBK, p.K, sA0);
     load_codes(nkf, c);
     expand_block(c, sB0);
@@ -365,13 +388,14 @@ __global__ __launch_bounds__(kThreads) void k_qgemm(QGemmArgs p) {
     const uint16_t* a2_base = p.A2 + m0 * p.lda2;
     const Rsrc rb2 = !kTransW ? rsrc(p.B2, p.K2 * p.ldb2 * 2)
                               : rsrc(p.B2 + n0 * p.ldb2, min((int64_t)kBN, p.N - n0) * p.ldb2 * 2);
+    constexpr int kChunks = kBN * kBK * 2 / 16 / kT;   // 16-byte chunks per thread
     for (int ls = 0; ls < nk2; ++ls) {
       const int64_t k0 = (int64_t)ls * kBK;
       dma_a(Checked{}, a2_base, (uint32_t)p.lda2 * 2u, k0, p.K2, sA0);
-      uint4 rb[4];
+      uint4 rb[kChunks];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int c = i * kThreads + t;        // 1024 chunks of 16 bytes
+      for (int i = 0; i < kChunks; ++i) {
+        const int c = i * kT + t;
         if (kTransW) {   // A rows n (128) × 8 chunks of k
           const int row = c >> 3, ch = c & 7;
           const int64_t gk = k0 + ch * 8;
@@ -383,14 +407,14 @@ __global__ __launch_bounds__(kThreads) void k_qgemm(QGemmArgs p) {
         }
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int c = i * kThreads + t;
+      for (int i = 0; i < kChunks; ++i) {
+        const int c = i * kT + t;
         if (kTransW) {
           const int row = c >> 3, ch = c & 7;
           *reinterpret_cast<uint4*>(sB0 + row * kBK + ((ch ^ swz(row)) << 3)) = rb[i];
         } else {
           const int kr = c >> 4, ch = c & 15;
-          *reinterpret_cast<uint4*>(sB0 + kr * kBN + ((ch ^ ((kr & 3) << 1)) << 3)) = rb[i];
+          *reinterpret_cast<uint4*>(sB0 + kr * kBN + ((ch ^ ((kr & 3) << 2)) << 3)) = rb[i];
         }
       }
       plain_step(ATag{});
@@ -401,12 +425,12 @@ __global__ __launch_bounds__(kThreads) void k_qgemm(QGemmArgs p) {
   // columns 8(e/4) + 4(lane/32) + e%4: four consecutive columns per 8-byte store
   const Rsrc rcout = rsrc(p.C + m0 * p.ldc, (int64_t)mrows * p.ldc * 2);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kI; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int row = wq * 128 + i * 32 + (lane & 31);
+        const int row = wq * kWR + i * 32 + (lane & 31);
         const int64_t col = n0 + j * 32 + q * 8 + (lane >> 5) * 4;
         const uint32_t off = col < p.N ? (uint32_t)((row * p.ldc + col) * 2) : kOobOff;
         const uint32_t lo = pack_bf16x2(acc[i][j][4 * q + 0], acc[i][j][4 * q + 1]);
@@ -427,9 +451,9 @@ hipError_t launch_qgemm(bool trans_w, const uint16_t* A, int64_t lda, const uint
               host_codebook()};
   const unsigned tiles = (unsigned)(((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN));
   if (trans_w)
-    hipLaunchKernelGGL(k_qgemm<true>, dim3(tiles), dim3(kThreads), 0, st, p);
+    hipLaunchKernelGGL((k_qgemm<true, kWaves>), dim3(tiles), dim3(64 * kWaves), 0, st, p);
   else
-    hipLaunchKernelGGL(k_qgemm<false>, dim3(tiles), dim3(kThreads), 0, st, p);
+    hipLaunchKernelGGL((k_qgemm<false, kWaves>), dim3(tiles), dim3(64 * kWaves), 0, st, p);
   return hipGetLastError();
 }
 
