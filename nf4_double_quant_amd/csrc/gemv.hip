@@ -47,14 +47,23 @@ __global__ __launch_bounds__(256) void k_lora_down_small(const uint16_t* __restr
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int64_t k0 = (int64_t)blockIdx.x * kPrepK;
   const int c0 = blockIdx.y * 64;
-  // stage A[k0:k0+512][c0:c0+64] (zeros outside)
-  for (int i = t; i < kPrepK * 8; i += 256) {
-    const int row = i >> 3, ch = i & 7;
-    const int64_t k = k0 + row;
-    const int col = c0 + ch * 8;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (k < d && col < r) v = *reinterpret_cast<const uint4*>(A + k * r + col);
-    *reinterpret_cast<uint4*>(s_a + row * kPrepStride + ch * 8) = v;
+  // stage A[k0:k0+512][c0:c0+64] (zeros outside); all 16 loads of a thread
+  // are in flight before the first store
+  {
+    uint4 v[kPrepK * 8 / 256];
+#pragma unroll
+    for (int u = 0; u < kPrepK * 8 / 256; ++u) {
+      const int i = u * 256 + t, row = i >> 3, ch = i & 7;
+      const int64_t k = k0 + row;
+      const int col = c0 + ch * 8;
+      v[u] = make_uint4(0, 0, 0, 0);
+      if (k < d && col < r) v[u] = *reinterpret_cast<const uint4*>(A + k * r + col);
+    }
+#pragma unroll
+    for (int u = 0; u < kPrepK * 8 / 256; ++u) {
+      const int i = u * 256 + t, row = i >> 3, ch = i & 7;
+      *reinterpret_cast<uint4*>(s_a + row * kPrepStride + ch * 8) = v[u];
+    }
   }
   __syncthreads();
   f32x4 acc[4];
@@ -149,50 +158,89 @@ __device__ __forceinline__ bf16x8 expand8(const Lut& t, uint32_t w) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
+typedef __amdgpu_buffer_rsrc_t GRsrc;
+constexpr uint32_t kGOob = 0x7FFFFF00u;   // an offset every descriptor rejects
+
+// Range-checked buffer descriptor: loads past `bytes` read 0.
+__device__ __forceinline__ GRsrc grsrc(const void* base, int64_t bytes) {
+  const int64_t cap = 0x7FFFFFF0;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                           (int)(bytes < 0 ? 0 : (bytes > cap ? cap : bytes)),
+                                           0x00020000);
+}
+__device__ __forceinline__ uint4 gload16(GRsrc r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
+// One 4-block group of a wave: lane (n = lane%16, q = lane/16) holds block
+// 4·g + q of row n — 64 codes, its 8-bit scale and its group step.
+struct GemvCodes {
+  uint4 c0, c1;
+  uint32_t q8;
+  float step;
+};
+
 template <int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void k_gemv(GemvArgs p) {
   __shared__ float s_part[WAVES][16][17];
   __shared__ float s_T[16 * kMaxGemvRank];
+  __shared__ float s_B[kMaxGemvRank * 16];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int64_t n0 = (int64_t)blockIdx.x * 16;
-  const int64_t nblk = p.d / kBlock;
-  const int64_t ngrp = (nblk + 3) / 4;
-  const int64_t n = n0 + (lane & 15);
-  const int m = lane & 15;
-  const bool row_ok = n < p.o;
-  const bool m_ok = m < p.M;
-
-  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int64_t gi = w; gi < ngrp; gi += WAVES) {
-    const int64_t kb = gi * 4 + (lane >> 4);
-    const bool ok = row_ok && kb < nblk;
-    uint4 c0 = make_uint4(0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u), c1 = c0;
-    float chat = 0.0f;
-    if (ok) {
-      const int64_t b = n * nblk + kb;
-      const uint4* cp = reinterpret_cast<const uint4*>(p.codes + b * (kBlock / 2));
-      c0 = cp[0];
-      c1 = cp[1];
-      chat = (float)p.scale8[b] * p.scale2[b / kGroup];
-    }
-    Lut lut;
-    build_lut(p.cb, chat, lut);
-    const uint4* xp = reinterpret_cast<const uint4*>(p.X + (int64_t)m * p.d + kb * kBlock);
-    const bool xok = m_ok && kb < nblk;
-    const uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint4 xv = xok ? xp[j] : make_uint4(0, 0, 0, 0);
-      const bf16x8 a = __builtin_bit_cast(bf16x8, xv);
-      const bf16x8 bw = expand8(lut, cw[j]);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bw, acc, 0, 0, 0);
-    }
-  }
-  // lane holds rows m = 4*(lane/16) + v of column n = lane%16
-#pragma unroll
-  for (int v = 0; v < 4; ++v) s_part[w][4 * (lane >> 4) + v][lane & 15] = acc[v];
-
+  const uint32_t nblk = (uint32_t)(p.d / kBlock);
+  const uint32_t ngrp = (nblk + 3) / 4;
+  const int nl = lane & 15, q = lane >> 4, m = lane & 15;
+  const int64_t n = n0 + nl;
   const bool lora = p.r > 0 && p.s != 0.0f;
+
+  // ---- weight stream.  Every offset is 32-bit (the host bounds the weight
+  // count); rows past o and blocks past the row end read 0 (a zero table
+  // and zero activations contribute nothing).
+  const uint32_t nbt = (uint32_t)(p.o * nblk);            // blocks in Wq
+  const GRsrc rc = grsrc(p.codes, (int64_t)nbt * 32);
+  const GRsrc rs8 = grsrc(p.scale8, nbt);
+  const GRsrc rs2 = grsrc(p.scale2, (int64_t)((nbt + kGroup - 1) / kGroup) * 4);
+  const GRsrc rx = grsrc(p.X, (int64_t)p.M * p.d * 2);
+  const bool row_ok = n < p.o;
+  const uint32_t brow = row_ok ? (uint32_t)n * nblk : 0u;
+  // groups of this wave: g = w, w + WAVES, ...; iterations past the end read 0
+  const int niter = (int)ngrp > w ? ((int)ngrp - w + WAVES - 1) / WAVES : 0;
+  auto load_codes = [&](int it, GemvCodes& c) {
+    const uint32_t kb = (uint32_t)(w + it * WAVES) * 4 + q;
+    const bool ok = row_ok && kb < nblk;
+    const uint32_t b = brow + kb;
+    c.c0 = gload16(rc, ok ? b * 32 : kGOob);
+    c.c1 = gload16(rc, ok ? b * 32 + 16 : kGOob);
+    c.q8 = __builtin_amdgcn_raw_buffer_load_b8(rs8, (int)(ok ? b : kGOob), 0, 0);
+    c.step = __builtin_bit_cast(
+        float, __builtin_amdgcn_raw_buffer_load_b32(rs2, (int)(ok ? (b / kGroup) * 4 : kGOob), 0, 0));
+  };
+  auto load_x = [&](int it, uint4 (&x)[8]) {
+    const uint32_t kb = (uint32_t)(w + it * WAVES) * 4 + q;
+    const bool ok = m < p.M && kb < nblk;
+    const uint32_t o0 = ok ? ((uint32_t)m * (uint32_t)p.d + kb * kBlock) * 2 : kGOob;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = gload16(rx, o0 + 16 * j);
+  };
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  auto compute = [&](const GemvCodes& c, const uint4 (&x)[8]) {
+    Lut lut;
+    build_lut(p.cb, (float)c.q8 * c.step, lut);   // ĉ = fl32(q8·step)
+    const uint32_t cw[8] = {c.c0.x, c.c0.y, c.c0.z, c.c0.w, c.c1.x, c.c1.y, c.c1.z, c.c1.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x[j]), expand8(lut, cw[j]),
+                                                    acc, 0, 0, 0);
+  };
+  // codes of four groups in flight, activations of two (branch-free: the
+  // steps past niter load and multiply zeros)
+  GemvCodes c0, c1, c2, c3;
+  uint4 xa[8], xb[8];
+  load_codes(0, c0); load_codes(1, c1); load_codes(2, c2); load_codes(3, c3);
+  load_x(0, xa);
+  // ---- the adapter pieces the epilogue needs, fetched after the first
+  // weight loads are in flight so their latency overlaps: T (summed over
+  // its split-K planes, fixed order) and B[:, n0:n0+16]
   if (lora || (p.T_out != nullptr && blockIdx.x == 0)) {
     for (int i = t; i < p.M * p.r; i += WAVES * 64) {
       float sum = 0.0f;
@@ -201,17 +249,43 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(GemvArgs p) {
       if (p.T_out != nullptr && blockIdx.x == 0) p.T_out[i] = sum;
     }
   }
+  if (lora) {
+    for (int i = t; i < p.r * 16; i += WAVES * 64) {
+      const int j = i >> 4, c = i & 15;
+      s_B[i] = n0 + c < p.o ? bf16_to_f32(p.B[(int64_t)j * p.o + n0 + c]) : 0.0f;
+    }
+  }
+
+  for (int it = 0; it < niter; it += 4) {
+    load_x(it + 1, xb);
+    compute(c0, xa);
+    load_codes(it + 4, c0);
+    load_x(it + 2, xa);
+    compute(c1, xb);
+    load_codes(it + 5, c1);
+    if (it + 2 < niter) {
+      load_x(it + 3, xb);
+      compute(c2, xa);
+      load_codes(it + 6, c2);
+      load_x(it + 4, xa);
+      compute(c3, xb);
+      load_codes(it + 7, c3);
+    }
+  }
+  // lane holds rows m = 4*(lane/16) + v of column n = lane%16
+#pragma unroll
+  for (int v = 0; v < 4; ++v) s_part[w][4 * (lane >> 4) + v][lane & 15] = acc[v];
   __syncthreads();
   if (t < 256) {
-    const int mm = t >> 4, nl = t & 15;
-    const int64_t nn = n0 + nl;
+    const int mm = t >> 4, nc = t & 15;
+    const int64_t nn = n0 + nc;
     if (mm < p.M && nn < p.o) {
       float y = 0.0f;
 #pragma unroll
-      for (int ww = 0; ww < WAVES; ++ww) y += s_part[ww][mm][nl];
+      for (int ww = 0; ww < WAVES; ++ww) y += s_part[ww][mm][nc];
       if (lora) {
         float l = 0.0f;
-        for (int j = 0; j < p.r; ++j) l += s_T[mm * p.r + j] * bf16_to_f32(p.B[(int64_t)j * p.o + nn]);
+        for (int j = 0; j < p.r; ++j) l += s_T[mm * p.r + j] * s_B[j * 16 + nc];
         y += p.s * l;
       }
       p.Y[(int64_t)mm * p.o + nn] = bf16_bits(y);
@@ -235,10 +309,12 @@ hipError_t launch_gemv_fwd(const uint16_t* X, int M, int64_t d, const uint8_t* c
   }
   GemvArgs p{X, codes, scale8, scale2, Tpart, B, Y, T_out, d, o, M, rr, ts, s, host_codebook()};
   const unsigned grid = (unsigned)((o + 15) / 16);
+  // enough waves to keep every CU streaming: split the reduction 4 ways
+  // when there are many row groups, 8 ways otherwise
   if (o >= 16 * 512)
     hipLaunchKernelGGL(k_gemv<4>, dim3(grid), dim3(256), 0, st, p);
   else
-    hipLaunchKernelGGL(k_gemv<16>, dim3(grid), dim3(1024), 0, st, p);
+    hipLaunchKernelGGL(k_gemv<8>, dim3(grid), dim3(512), 0, st, p);
   return hipGetLastError();
 }
 
