@@ -59,12 +59,15 @@ extern "C" {
 #define QLORA_BLOCK 64      /* weights per first-level (absmax) block        */
 #define QLORA_GROUP 256     /* first-level constants per second-level step   */
 #define QLORA_MAX_RANK 256  /* largest LoRA rank r accepted                  */
+#define QLORA_MAX_DIM (1LL << 20)       /* largest d and o of a linear layer  */
+#define QLORA_MAX_WEIGHTS (1LL << 31)   /* largest o*d of a linear layer      */
 
 typedef enum {
   QLORA_OK = 0,
   QLORA_E_INVALID = 1,    /* null pointer where one is required, bad enum, n < 0 */
   QLORA_E_SHAPE = 2,      /* d % 64 != 0, r out of range or not a multiple of 8,
-                             negative sizes, n != o*d                          */
+                             negative sizes, n != o*d, d or o above
+                             QLORA_MAX_DIM, o*d above QLORA_MAX_WEIGHTS      */
   QLORA_E_ALIGN = 3,      /* a tensor pointer is not 16-byte aligned          */
   QLORA_E_WORKSPACE = 4,  /* ws_bytes below qlora_workspace_bytes()          */
   QLORA_E_NO_DEVICE = 5,  /* no HIP device visible to the process            */

@@ -122,6 +122,9 @@ int check_quant_view(const qlora_nf4dq* q) {
 
 int check_linear_shapes(int64_t M, int64_t d, int64_t o, int64_t r, const qlora_nf4dq* W) {
   if (M < 0 || d <= 0 || o <= 0 || r < 0) return QLORA_E_SHAPE;
+  // the kernels address a weight tensor and a 512-row activation tile with
+  // 32-bit offsets
+  if (d > QLORA_MAX_DIM || o > QLORA_MAX_DIM || o * d > QLORA_MAX_WEIGHTS) return QLORA_E_SHAPE;
   if (d % QLORA_BLOCK != 0 || o % 8 != 0) return QLORA_E_SHAPE;
   if (r > QLORA_MAX_RANK || r % 8 != 0) return QLORA_E_SHAPE;
   int st = check_quant_view(W);
@@ -160,7 +163,7 @@ const char* qlora_strerror(int status) {
   switch (status) {
     case QLORA_OK: return "ok";
     case QLORA_E_INVALID: return "invalid argument";
-    case QLORA_E_SHAPE: return "unsupported shape (need d % 64 == 0, o % 8 == 0, 0 <= r <= 256, r % 8 == 0, n == o*d)";
+    case QLORA_E_SHAPE: return "unsupported shape (need d % 64 == 0, o % 8 == 0, 0 <= r <= 256, r % 8 == 0, n == o*d, d and o <= 2^20, o*d <= 2^31)";
     case QLORA_E_ALIGN: return "tensor pointer not 16-byte aligned";
     case QLORA_E_WORKSPACE: return "workspace too small";
     case QLORA_E_NO_DEVICE: return "no HIP device available";

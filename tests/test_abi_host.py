@@ -101,6 +101,9 @@ def test_validation_statuses(L):
     assert call(r=12) == 2                                  # r % 8
     assert call(r=264) == 2                                 # r > 256
     assert call(view=_view(128 * 127)) == 2                 # n != o*d
+    big = (1 << 20) + 64                                    # d above the 32-bit offset limit
+    assert call(d=big, view=_view(128 * big)) == 2
+    assert call(o=1 << 20, d=4096, view=_view((1 << 20) * 4096)) == 2   # o*d above 2^31
     assert call(X=A16 + 2) == 3                             # alignment
     assert call(view=_view(128 * 128, codes=A16 + 4)) == 3
     assert call(wsb=16) == 4                                # workspace
