@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--pmc", action="store_true",
                     help="short run for hardware-counter passes: a 256 MiB device copy "
                          "(calibration of FETCH_SIZE/WRITE_SIZE) and --steps steps, no timing")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn the counter_collection.csv files of a FETCH_SIZE pass and a "
+                         "WRITE_SIZE pass of --pmc into " + os.path.relpath(PROFILE_PMC, ROOT))
     return ap.parse_args()
 
 
@@ -59,12 +62,51 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def pmc_summary(fetch_csv: str, write_csv: str, workload: str) -> dict:
+    """HBM bytes per k_qgemm launch from a FETCH_SIZE and a WRITE_SIZE pass.
+
+    Each counter (KiB per dispatch) is scaled by the ratio of the known bytes
+    of the calibration kernel (256 MiB read, 256 MiB written) to what the same
+    counter reports for it in the same pass.
+    """
+    import csv
+
+    def rows(path, counter):
+        with open(path) as f:
+            return [r for r in csv.DictReader(f) if r["Counter_Name"] == counter]
+
+    out = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rs = rows(path, counter)
+        cal = [float(r["Counter_Value"]) for r in rs if "MulFunctor" in r["Kernel_Name"]]
+        main = [float(r["Counter_Value"]) for r in rs if "k_qgemm" in r["Kernel_Name"]]
+        if not cal or not main:
+            raise SystemExit(f"{path}: no calibration or k_qgemm dispatches for {counter}")
+        cal_kib = statistics.median(cal)
+        factor = (256 << 20) / (cal_kib * 1024.0)
+        out[counter] = {"calibration_kib": cal_kib, "factor": factor,
+                        "k_qgemm_kib_per_dispatch": statistics.mean(main), "dispatches": len(main)}
+    fetch = out["FETCH_SIZE"]["k_qgemm_kib_per_dispatch"] * 1024 * out["FETCH_SIZE"]["factor"]
+    write = out["WRITE_SIZE"]["k_qgemm_kib_per_dispatch"] * 1024 * out["WRITE_SIZE"]["factor"]
+    return {"workload": workload, "kernel": "k_qgemm (forward and backward launches averaged)",
+            "kernel_source_hash": kernel_source_hash(), "counters": out,
+            "hbm_fetch_bytes_per_launch": round(fetch), "hbm_write_bytes_per_launch": round(write),
+            "hbm_bytes_per_launch": round(fetch + write)}
+
+
 def step_flops(M, d, o, r):
     return 4 * M * d * o + 6 * M * r * (d + o)
 
 
 def main():
     args = parse()
+    if args.pmc_summary:
+        res = pmc_summary(*args.pmc_summary, workload=args.workload)
+        with open(PROFILE_PMC, "w") as f:
+            json.dump(res, f, indent=1)
+            f.write("\n")
+        print(json.dumps(res))
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -99,11 +141,12 @@ def main():
         qb.qlora_linear_bwd(dY, X, T, q, A, B, s, ws=ws_b)
 
     if args.pmc:
-        # calibration: a plain copy of exactly 256 MiB (read 256 MiB, write 256 MiB)
+        # calibration: an elementwise kernel that reads exactly 256 MiB and
+        # writes exactly 256 MiB (torch's MulFunctor kernel)
         src = torch.empty(64 << 20, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
         for _ in range(3):
-            dst.copy_(src)
+            torch.mul(src, 1.0, out=dst)
         for _ in range(args.steps):
             step()
         torch.cuda.synchronize()
@@ -224,25 +267,55 @@ def bench_decode(args, qb, torch, np, synth, dev):
                 A, B = adapters[p.name]
                 qb.qlora_linear_fwd(xs[p.name], qw, A, B, wl.s, want_T=False, ws=ws, out=ys[p.name])
 
-        for layer in sets[:4]:
+        for layer in sets:
             one(layer)
         torch.cuda.synchronize()
         reps = max(2, 96 // len(sets))
+        # per-launch kernel time of the dequant-GEMV (eager, HIP events on the stream)
         qb.qlora_timing_begin([qb.K_GEMV])
+        for layer in sets:
+            one(layer)
+        torch.cuda.synchronize()
+        qb.qlora_timing_end()
+        gemv_ms, gemv_n = qb.qlora_timing_read(qb.K_GEMV)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        # eager: one Python call per projection (host launch cost included)
         e0.record()
         for _ in range(reps):
             for layer in sets:
                 one(layer)
         e1.record()
         torch.cuda.synchronize()
-        qb.qlora_timing_end()
-        n = reps * len(sets)
-        us = e0.elapsed_time(e1) * 1e3 / n
-        gemv_ms, gemv_n = qb.qlora_timing_read(qb.K_GEMV)
-        res[f"M{M}"] = {"us_per_mlp": round(us, 2), "bytes_per_mlp": byts,
-                        "GBps": round(byts / (us * 1e-6) / 1e9, 1),
-                        "frac_of_hbm": round(byts / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+        us_eager = e0.elapsed_time(e1) * 1e3 / (reps * len(sets))
+        # the same launches captured once in a HIP graph and replayed: the GPU time
+        us, graph_ok = None, None
+        try:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for layer in sets:
+                    one(layer)
+            for _ in range(2):
+                g.replay()
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(reps):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / (reps * len(sets))
+            # every replay leaves the last set's outputs: compare with eager calls
+            got = {k: v.clone() for k, v in ys.items()}
+            one(sets[-1])
+            torch.cuda.synchronize()
+            graph_ok = all(torch.equal(got[k], ys[k]) for k in ys)
+        except Exception as e:  # capture unsupported: report the eager figure only
+            print(f"decode graph capture failed: {e}", file=sys.stderr)
+        t = us if (us is not None and graph_ok) else us_eager
+        res[f"M{M}"] = {"us_per_mlp": round(t, 2), "timing": "hip_graph" if t is us else "eager",
+                        "us_per_mlp_eager": round(us_eager, 2), "graph_replay_matches_eager": graph_ok,
+                        "bytes_per_mlp": byts,
+                        "GBps": round(byts / (t * 1e-6) / 1e9, 1),
+                        "frac_of_hbm": round(byts / (t * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
                         "gemv_kernel_us": round(gemv_ms * 1e3 / max(gemv_n, 1), 2) if gemv_n else None}
     return {"workload": "decode_mlp_7b: gate/up 4096->11008, down 11008->4096, r=16, fwd only",
             "weight_sets_cycled": len(sets), "peak_GBps": PEAK_HBM_GBPS, **res}
