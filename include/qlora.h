@@ -40,8 +40,9 @@
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL means
  *     the null stream).  Nothing synchronizes the host.
  *   - Calls that share a workspace must be ordered (same stream); calls with
- *     separate workspaces are independent.  No kernel uses atomics, so every
- *     result is bitwise reproducible run to run.
+ *     separate workspaces are independent.  No kernel uses atomics; split
+ *     planes are summed in plane order, so every result is bitwise
+ *     reproducible run to run.
  *
  * Errors: every entry point returns a qlora_status.  Argument checks happen
  * before anything is launched; on error nothing was enqueued.

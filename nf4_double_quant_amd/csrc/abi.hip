@@ -304,10 +304,9 @@ int qlora_linear_bwd(const qlora_bf16* dY, const qlora_bf16* X, const float* T, 
   const bool lora = r > 0 && s != 0.0f;
 
   if (r > 0) {
-    // s·T in bf16, the operand of dB = (s·T)ᵀ·dY
-    if (T != nullptr) {
-      QL_RUN(QLORA_K_ADAPTER, hs, launch_scale_to_bf16(T, M * r, s, sT, hs));
-    } else {
+    // T when the caller did not keep it: s·T in bf16 from the planes.  A
+    // given T enters dB's kernel as fp32, scaled and rounded to bf16 there.
+    if (T == nullptr) {
       QL_RUN(QLORA_K_ADAPTER, hs, launch_rank_down(false, X, M, d, A, (int)r, Tpart, hs));
       QL_RUN(QLORA_K_ADAPTER, hs,
              launch_reduce_planes(Tpart, (int)L.t_splits, M * r, M * r, nullptr, sT, s, hs));
@@ -317,8 +316,11 @@ int qlora_linear_bwd(const qlora_bf16* dY, const qlora_bf16* X, const float* T, 
     QL_RUN(QLORA_K_ADAPTER, hs,
            launch_reduce_planes(Upart, (int)L.u_splits, M * r, M * r, nullptr, sU, s, hs));
     // dA = Xᵀ·(s·U) [d][r] and dB = (s·T)ᵀ·dY [r][o], reductions over the tokens
-    QL_RUN(QLORA_K_GRADS, hs, launch_rank_grad(true, X, d, sU, (int)r, M, dApart, hs));
-    QL_RUN(QLORA_K_GRADS, hs, launch_rank_grad(false, dY, o, sT, (int)r, M, dBpart, hs));
+    QL_RUN(QLORA_K_GRADS, hs, launch_rank_grad(true, X, d, sU, false, 1.0f, (int)r, M, dApart, hs));
+    if (T != nullptr)
+      QL_RUN(QLORA_K_GRADS, hs, launch_rank_grad(false, dY, o, T, true, s, (int)r, M, dBpart, hs));
+    else
+      QL_RUN(QLORA_K_GRADS, hs, launch_rank_grad(false, dY, o, sT, false, 1.0f, (int)r, M, dBpart, hs));
     QL_RUN(QLORA_K_GRADS, hs,
            launch_reduce_planes(dApart, (int)L.g_splits, d * r, d * r, nullptr, dA, 1.0f, hs));
     QL_RUN(QLORA_K_GRADS, hs,

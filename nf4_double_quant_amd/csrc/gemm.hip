@@ -1,5 +1,5 @@
 // Small elementwise kernels of the adapter path: the fixed-order sum of
-// split-K planes, fp32 -> scaled bf16, and zero fill.
+// split planes and zero fill.
 #include "kernels.h"
 
 namespace qlora {
@@ -36,13 +36,6 @@ __global__ __launch_bounds__(256) void k_fill_zero_bf16(uint16_t* __restrict__ y
 }
 
 // fp32 -> bf16(scale·x), elementwise.
-__global__ __launch_bounds__(256) void k_scale_to_bf16(const float* __restrict__ x, int64_t n,
-                                                       float scale, uint16_t* __restrict__ y) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-       i += (int64_t)gridDim.x * blockDim.x)
-    y[i] = bf16_bits(scale * x[i]);
-}
-
 // ------------------------------------------------------------------ launchers
 hipError_t launch_reduce_planes(const float* part, int splits, int64_t plane, int64_t count,
                                 float* out_f32, uint16_t* out_bf16, float scale, hipStream_t st) {
@@ -51,15 +44,6 @@ hipError_t launch_reduce_planes(const float* part, int splits, int64_t plane, in
   if (blocks > 4096) blocks = 4096;
   hipLaunchKernelGGL(k_reduce_planes, dim3((unsigned)blocks), dim3(256), 0, st, part, splits,
                      plane, count, out_f32, out_bf16, scale);
-  return hipGetLastError();
-}
-
-hipError_t launch_scale_to_bf16(const float* x, int64_t n, float scale, uint16_t* y,
-                                hipStream_t st) {
-  if (n == 0) return hipSuccess;
-  int64_t blocks = (n + 255) / 256;
-  if (blocks > 8192) blocks = 8192;
-  hipLaunchKernelGGL(k_scale_to_bf16, dim3((unsigned)blocks), dim3(256), 0, st, x, n, scale, y);
   return hipGetLastError();
 }
 

@@ -13,7 +13,9 @@
 //    operands are token-major, staged in LDS as [m][·] rows and gathered
 //    with ds_read_b64_tr_b16 (4 consecutive tokens of one column per read).
 // Split planes are summed in a fixed order by k_reduce_planes, so results
-// are bitwise reproducible.
+// are bitwise reproducible.  (Summing them inside these kernels, with the
+// last workgroup of a tile reducing, costs more on this chip: every
+// device-scope release fence writes back the XCD's whole L2.)
 #include "kernels.h"
 
 namespace qlora {
@@ -52,7 +54,8 @@ constexpr uint32_t kOob = 0x7FFFFFF0u;   // an offset every descriptor rejects
 
 constexpr int kDownRows = 128;    // rows of P per workgroup (4 waves × 32)
 constexpr int kDownK = 512;       // k-slice per workgroup
-constexpr int kDownLd = 80;       // LDS row stride (bf16) of the Q tile: 64 + 16 pad
+constexpr int kDownLd = 80;       // LDS row stride (bf16) of the [k][j] Q tile: 64 + 16 pad
+constexpr int kDownKLd = kDownK + 8;   // LDS row stride (bf16) of the [j][k] Q tile
 
 }  // namespace
 
@@ -63,7 +66,7 @@ template <bool kQRowMajorK>
 __global__ __launch_bounds__(256) void k_rank_down(const uint16_t* __restrict__ P, int64_t M,
                                                    int64_t K, const uint16_t* __restrict__ Q,
                                                    int r, float* __restrict__ part) {
-  __shared__ __attribute__((aligned(16))) uint16_t s_q[kQRowMajorK ? 8 : kDownK * kDownLd];
+  __shared__ __attribute__((aligned(16))) uint16_t s_q[kQRowMajorK ? 64 * kDownKLd : kDownK * kDownLd];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int64_t m0 = (int64_t)blockIdx.x * kDownRows;
   const int64_t k0 = (int64_t)blockIdx.y * kDownK;
@@ -71,18 +74,42 @@ __global__ __launch_bounds__(256) void k_rank_down(const uint16_t* __restrict__ 
   const int64_t kn = min((int64_t)kDownK, K - k0);       // valid k in this slice (multiple of 8)
 
   if (!kQRowMajorK) {
-    // stage Q[k0:k0+512][c0:c0+64]; rows past K and columns past r read 0
+    // stage Q[k0:k0+512][c0:c0+64]; rows past K and columns past r read 0.
+    // All 16 loads of a thread are in flight before the first store.
     const Rsrc rq = rsrc(Q + k0 * r, kn * r * 2);
-    for (int i = t; i < kDownK * 8; i += 256) {
-      const int row = i >> 3, col = c0 + (i & 7) * 8;
-      const uint4 v = bload16(rq, col < r ? (uint32_t)((row * r + col) * 2) : kOob);
-      *reinterpret_cast<uint4*>(s_q + row * kDownLd + (i & 7) * 8) = v;
+    uint4 v[kDownK * 8 / 256];
+#pragma unroll
+    for (int u = 0; u < kDownK * 8 / 256; ++u) {
+      const int i = u * 256 + t, row = i >> 3, col = c0 + (i & 7) * 8;
+      v[u] = bload16(rq, col < r ? (uint32_t)((row * r + col) * 2) : kOob);
+    }
+#pragma unroll
+    for (int u = 0; u < kDownK * 8 / 256; ++u) {
+      const int i = u * 256 + t;
+      *reinterpret_cast<uint4*>(s_q + (i >> 3) * kDownLd + (i & 7) * 8) = v[u];
+    }
+    __syncthreads();
+  } else {
+    // stage Q[c0:c0+64][k0:k0+512] (rows j of B, K-major); rows past r and
+    // columns past K read 0.  Row stride 1040 bytes: the 16 rows one
+    // ds_read_b128 touches fall in different banks.
+    const Rsrc rq = rsrc(Q + k0, ((int64_t)(r - 1) * K + kn) * 2);
+    uint4 v[64 * kDownK / 8 / 256];
+#pragma unroll
+    for (int u = 0; u < 64 * kDownK / 8 / 256; ++u) {
+      const int i = u * 256 + t, row = i >> 6, ch = i & 63;     // 64 rows × 64 chunks
+      const int j = c0 + row, kk = ch * 8;
+      v[u] = bload16(rq, (j < r && kk < kn) ? (uint32_t)(((int64_t)j * K + kk) * 2) : kOob);
+    }
+#pragma unroll
+    for (int u = 0; u < 64 * kDownK / 8 / 256; ++u) {
+      const int i = u * 256 + t;
+      *reinterpret_cast<uint4*>(s_q + (i >> 6) * kDownKLd + (i & 63) * 8) = v[u];
     }
     __syncthreads();
   }
   const int64_t mrows = min((int64_t)kDownRows, M - m0);
   const Rsrc rp = rsrc(P + m0 * K + k0, mrows > 0 ? ((mrows - 1) * K + kn) * 2 : 0);
-  const Rsrc rqk = rsrc(Q + k0, kQRowMajorK ? ((int64_t)(r - 1) * K + kn) * 2 : 0);
 
   f32x4 acc[2][4];
 #pragma unroll
@@ -91,28 +118,32 @@ __global__ __launch_bounds__(256) void k_rank_down(const uint16_t* __restrict__ 
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
   const int g = lane >> 4, l16 = lane & 15;
-  for (int kq = 0; kq < kDownK / 32; ++kq) {
+  // P fragments for 32-wide step kq are loaded kPre steps ahead, so memory
+  // latency overlaps the MFMAs.
+  constexpr int kSteps = kDownK / 32, kPre = 3;
+  bf16x8 a[kSteps][2];
+  auto load = [&](int kq) {
     const int kk = kq * 32 + 8 * g;                // this lane's 8 k, relative to k0
-    bf16x8 a[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int row = w * 32 + i * 16 + l16;
       const uint32_t off = kk < kn ? (uint32_t)((row * K + kk) * 2) : kOob;
-      a[i] = __builtin_bit_cast(bf16x8, bload16(rp, off));
+      a[kq][i] = __builtin_bit_cast(bf16x8, bload16(rp, off));
     }
+  };
+#pragma unroll
+  for (int kq = 0; kq < kPre; ++kq) load(kq);
+#pragma unroll
+  for (int kq = 0; kq < kSteps; ++kq) {
+    if (kq + kPre < kSteps) load(kq + kPre);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      bf16x8 b;
-      if (kQRowMajorK) {
-        const int col = c0 + j * 16 + l16;
-        const uint32_t off = (kk < kn && col < r) ? (uint32_t)((col * K + kk) * 2) : kOob;
-        b = __builtin_bit_cast(bf16x8, bload16(rqk, off));
-      } else {
-        b = frag_tr(s_q, kDownLd, kq * 32, j * 16, lane);
-      }
+      const bf16x8 b =
+          kQRowMajorK ? *reinterpret_cast<const bf16x8*>(s_q + (j * 16 + l16) * kDownKLd + kq * 32 + 8 * g)
+                      : frag_tr(s_q, kDownLd, kq * 32, j * 16, lane);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b, acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[kq][i], b, acc[i][j], 0, 0, 0);
     }
   }
   // lane holds rows 4*(lane/16)+v of column lane%16 in each 16×16 block
@@ -140,10 +171,11 @@ constexpr int kSmallLd = 64 + 16;
 // part[z][...] = Σ_{m in slice z} BIG[m][p]·SMALL[m][j] for p in a 128-wide
 // tile and j in [64 c, 64 c + 64).  kOutPJ: stored as [p][j] (row length r),
 // else as [j][p] (row length P).
-template <bool kOutPJ>
+// kSmallF32: SMALL is fp32 and enters as bf16(small_scale · SMALL).
+template <bool kOutPJ, bool kSmallF32>
 __global__ __launch_bounds__(256) void k_rank_grad(const uint16_t* __restrict__ big, int64_t P,
-                                                   const uint16_t* __restrict__ small, int r,
-                                                   int64_t M, float* __restrict__ part) {
+                                                   const void* __restrict__ small, float small_scale,
+                                                   int r, int64_t M, float* __restrict__ part) {
   __shared__ __attribute__((aligned(16))) uint16_t s_big[kGradChunk * kBigLd];
   __shared__ __attribute__((aligned(16))) uint16_t s_small[kGradChunk * kSmallLd];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
@@ -152,7 +184,8 @@ __global__ __launch_bounds__(256) void k_rank_grad(const uint16_t* __restrict__ 
   const int c0 = blockIdx.z * 64;
   const int64_t mlen = min((int64_t)kGradM, M - mz);
   const Rsrc rb = rsrc(big + mz * P, mlen * P * 2);
-  const Rsrc rs = rsrc(small + mz * r, mlen * r * 2);
+  const Rsrc rs = rsrc(static_cast<const char*>(small) + mz * r * (kSmallF32 ? 4 : 2),
+                      mlen * r * (kSmallF32 ? 4 : 2));
 
   f32x4 acc[2][4];
 #pragma unroll
@@ -160,33 +193,54 @@ __global__ __launch_bounds__(256) void k_rank_grad(const uint16_t* __restrict__ 
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  for (int mc = 0; mc < kGradM; mc += kGradChunk) {
-    // stage BIG[mc:mc+64][p0:p0+128] and SMALL[mc:mc+64][c0:c0+64]
-    uint4 vb[4], vs[2];
+  // BIG[mc:mc+64][p0:p0+128] and SMALL[mc:mc+64][c0:c0+64] of chunk c go
+  // through registers into LDS; the loads of chunk c+1 are issued before the
+  // MFMAs of chunk c, so memory latency overlaps them.
+  constexpr int kChunks = kGradM / kGradChunk;
+  constexpr int kSmallLoads = kSmallF32 ? 4 : 2;   // 16-byte loads per thread per chunk
+  uint4 vb[kChunks][4], vs[kChunks][kSmallLoads];
+  auto load = [&](int c) {
+    const int mc = c * kGradChunk;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int i = q * 256 + t;                 // 64 rows × 16 chunks
       const int row = i >> 4, ch = i & 15;
       const int64_t col = p0 + ch * 8;
-      vb[q] = bload16(rb, col < P ? (uint32_t)(((mc + row) * P + col) * 2) : kOob);
+      vb[c][q] = bload16(rb, col < P ? (uint32_t)(((mc + row) * P + col) * 2) : kOob);
     }
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int i = q * 256 + t;                 // 64 rows × 8 chunks
-      const int row = i >> 3, ch = i & 7;
-      const int col = c0 + ch * 8;
-      vs[q] = bload16(rs, col < r ? (uint32_t)(((mc + row) * r + col) * 2) : kOob);
+    for (int q = 0; q < kSmallLoads; ++q) {
+      const int i = q * 256 + t;
+      if (kSmallF32) {                           // 64 rows × 16 chunks of 4 fp32
+        const int row = i >> 4, col = c0 + (i & 15) * 4;
+        vs[c][q] = bload16(rs, col < r ? (uint32_t)(((mc + row) * r + col) * 4) : kOob);
+      } else {                                   // 64 rows × 8 chunks of 8 bf16
+        const int row = i >> 3, col = c0 + (i & 7) * 8;
+        vs[c][q] = bload16(rs, col < r ? (uint32_t)(((mc + row) * r + col) * 2) : kOob);
+      }
     }
+  };
+  load(0);
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    if (c + 1 < kChunks) load(c + 1);
     __syncthreads();   // previous round's fragments are consumed
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int i = q * 256 + t;
-      *reinterpret_cast<uint4*>(s_big + (i >> 4) * kBigLd + (i & 15) * 8) = vb[q];
+      *reinterpret_cast<uint4*>(s_big + (i >> 4) * kBigLd + (i & 15) * 8) = vb[c][q];
     }
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < kSmallLoads; ++q) {
       const int i = q * 256 + t;
-      *reinterpret_cast<uint4*>(s_small + (i >> 3) * kSmallLd + (i & 7) * 8) = vs[q];
+      if (kSmallF32) {
+        const float4 x = __builtin_bit_cast(float4, vs[c][q]);
+        const uint2 b = make_uint2(pack_bf16x2(small_scale * x.x, small_scale * x.y),
+                                   pack_bf16x2(small_scale * x.z, small_scale * x.w));
+        *reinterpret_cast<uint2*>(s_small + (i >> 4) * kSmallLd + (i & 15) * 4) = b;
+      } else {
+        *reinterpret_cast<uint4*>(s_small + (i >> 3) * kSmallLd + (i & 7) * 8) = vs[c][q];
+      }
     }
     __syncthreads();
 #pragma unroll
@@ -241,15 +295,20 @@ hipError_t launch_rank_down(bool q_rowmajor_k, const uint16_t* P, int64_t M, int
   return hipGetLastError();
 }
 
-hipError_t launch_rank_grad(bool out_pj, const uint16_t* big, int64_t P, const uint16_t* small,
-                            int r, int64_t M, float* part, hipStream_t st) {
+hipError_t launch_rank_grad(bool out_pj, const uint16_t* big, int64_t P, const void* small,
+                            bool small_f32, float small_scale, int r, int64_t M, float* part,
+                            hipStream_t st) {
   if (P == 0 || r == 0) return hipSuccess;
   dim3 grid((unsigned)((P + kGradP - 1) / kGradP), (unsigned)rank_grad_splits(M),
             (unsigned)((r + 63) / 64));
-  if (out_pj)
-    hipLaunchKernelGGL(k_rank_grad<true>, grid, dim3(256), 0, st, big, P, small, r, M, part);
-  else
-    hipLaunchKernelGGL(k_rank_grad<false>, grid, dim3(256), 0, st, big, P, small, r, M, part);
+#define QL_GRAD(PJ, F32) \
+  hipLaunchKernelGGL((k_rank_grad<PJ, F32>), grid, dim3(256), 0, st, big, P, small, small_scale, r, M, part)
+  if (out_pj) {
+    if (small_f32) QL_GRAD(true, true); else QL_GRAD(true, false);
+  } else {
+    if (small_f32) QL_GRAD(false, true); else QL_GRAD(false, false);
+  }
+#undef QL_GRAD
   return hipGetLastError();
 }
 

@@ -177,3 +177,30 @@ def test_decode_mlp_7b_full(proj):
         Yr, Tr = linear.forward(Xf, Wh, Af, Bf, wl.s)
         check_close(bf16_host_f64(Y), Yr, f"Y {proj} M={M}")
         check_close(T.cpu().numpy(), Tr, f"T {proj} M={M}")
+
+
+def test_workspace_reuse_across_shapes():
+    """One workspace serves calls of different shapes in turn and gives the
+    same bits as a fresh one; a given T and a recomputed T give the same
+    adapter gradients."""
+    ws = qb.Workspace()
+    shapes = ((600, 384, 520, 24, 11), (130, 1088, 264, 64, 12), (600, 384, 520, 24, 11))
+    outs = []
+    for M, d, o, r, seed in shapes:
+        W, X, A, B, dY = make_case(M, d, o, r, seed)
+        q = qb.qlora_quantize_nf4_dq(torch.from_numpy(W).cuda())
+        Xd, Ad, Bd, dYd = bf16_dev(X), bf16_dev(A), bf16_dev(B), bf16_dev(dY)
+        for with_T in (True, False):
+            Y, T = qb.qlora_linear_fwd(Xd, q, Ad, Bd, 2.0, ws=ws)
+            dX, dA, dB = qb.qlora_linear_bwd(dYd, Xd, T if with_T else None, q, Ad, Bd, 2.0, ws=ws)
+            torch.cuda.synchronize()
+            fresh = qb.Workspace()
+            Y2, _ = qb.qlora_linear_fwd(Xd, q, Ad, Bd, 2.0, ws=fresh)
+            dX2, dA2, dB2 = qb.qlora_linear_bwd(dYd, Xd, T if with_T else None, q, Ad, Bd, 2.0,
+                                               ws=fresh)
+            torch.cuda.synchronize()
+            for a, b in ((Y, Y2), (dX, dX2), (dA, dA2), (dB, dB2)):
+                assert torch.equal(a, b)
+        outs.append((Y.clone(), dX.clone(), dA.clone(), dB.clone()))
+    for a, b in zip(outs[0], outs[2]):
+        assert torch.equal(a, b)
