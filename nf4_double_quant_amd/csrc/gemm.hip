@@ -14,8 +14,17 @@ __global__ __launch_bounds__(256) void k_reduce_planes(const float* __restrict__
   const int64_t n4 = count / 4;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4;
        i += (int64_t)gridDim.x * blockDim.x) {
+    // planes summed in order, four loads in flight at a time
     float4 s = reinterpret_cast<const float4*>(part)[i];
-    for (int z = 1; z < splits; ++z) {
+    int z = 1;
+    for (; z + 4 <= splits; z += 4) {
+      float4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = reinterpret_cast<const float4*>(part + (int64_t)(z + u) * plane)[i];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) { s.x += v[u].x; s.y += v[u].y; s.z += v[u].z; s.w += v[u].w; }
+    }
+    for (; z < splits; ++z) {
       const float4 v = reinterpret_cast<const float4*>(part + (int64_t)z * plane)[i];
       s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
     }

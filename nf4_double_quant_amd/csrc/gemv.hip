@@ -242,9 +242,19 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(GemvArgs p) {
   // weight loads are in flight so their latency overlaps: T (summed over
   // its split-K planes, fixed order) and B[:, n0:n0+16]
   if (lora || (p.T_out != nullptr && blockIdx.x == 0)) {
+    const int64_t plane = (int64_t)p.M * p.r;
     for (int i = t; i < p.M * p.r; i += WAVES * 64) {
+      // planes summed in order, eight loads in flight at a time
       float sum = 0.0f;
-      for (int z = 0; z < p.tsplits; ++z) sum += p.Tpart[(int64_t)z * p.M * p.r + i];
+      int z = 0;
+      for (; z + 8 <= p.tsplits; z += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = p.Tpart[(int64_t)(z + u) * plane + i];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) sum += v[u];
+      }
+      for (; z < p.tsplits; ++z) sum += p.Tpart[(int64_t)z * plane + i];
       s_T[i] = sum;
       if (p.T_out != nullptr && blockIdx.x == 0) p.T_out[i] = sum;
     }
