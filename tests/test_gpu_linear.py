@@ -154,6 +154,31 @@ def test_full_linear_4096_sampled():
     check_close(T.cpu().numpy()[rows], Xf[rows] @ Af, "T rows")
 
 
+@pytest.mark.parametrize("pname", ["gate", "down"])
+def test_block_65b_projection_sampled(pname):
+    """65B-style shapes at their full size (gate 22016×8192, down 8192×22016,
+    2048 tokens, rank 64): sampled token rows of Y, dX and T, sampled rows of
+    dA and columns of dB, against the oracle's full dequantized weight."""
+    wl = synth.WORKLOADS["block_65b"]
+    p = next(pp for pp in wl.projs if pp.name == pname)
+    W, X, A, B, dY = synth.layer_inputs(wl, p)
+    Y, T, dX, dA, dB = run_gpu(W, X, A, B, dY, wl.s)
+    Wh = oracle_weight(W)
+    del W
+    Xf, Af, Bf, dYf = map(bf16_to_f64, (X, A, B, dY))
+    rng = np.random.default_rng(1)
+    rows = np.sort(rng.choice(wl.M, 24, replace=False))
+    rows[-1] = wl.M - 1
+    check_close(bf16_host_f64(Y)[rows], linear.forward_rows(Xf, Wh, Af, Bf, wl.s, rows), "Y rows")
+    check_close(bf16_host_f64(dX)[rows], linear.dx_rows(dYf, Wh, Af, Bf, wl.s, rows), "dX rows")
+    a_rows = np.sort(rng.choice(p.d, 64, replace=False))
+    b_cols = np.sort(rng.choice(p.o, 64, replace=False))
+    ga, gb = linear.grad_cols(dYf, Xf, Af, Bf, wl.s, a_rows, b_cols)
+    check_close(bf16_host_f64(dA)[a_rows], ga, "dA rows")
+    check_close(bf16_host_f64(dB)[:, b_cols], gb, "dB cols")
+    check_close(T.cpu().numpy()[rows], Xf[rows] @ Af, "T rows")
+
+
 @pytest.mark.parametrize("M", [1, 2, 4, 13, 16])
 @pytest.mark.parametrize("d,o,r", [(192, 264, 16), (640, 40, 8), (64, 8, 0), (128, 4104, 24)])
 def test_few_token_path(M, d, o, r):
