@@ -23,13 +23,14 @@
  *     linear entry points d must be a multiple of 64, so blocks run along d.
  *   - codes: 4 bits per weight, 8 consecutive codes per little-endian 32-bit
  *     word: byte j (0..3) holds code j in bits 3:0 and code j+4 in bits 7:4.
- *     Codes past n are padded with 7 (the zero code), so the buffer is
- *     4·ceil(n/8) bytes (n/2 when 8 divides n).
+ *     Codes past n are padded with 7 (NF4's zero code; 7 for every table),
+ *     so the buffer is 4·ceil(n/8) bytes (n/2 when 8 divides n).
  *   - scale8: ceil(n/64) bytes, unsigned linear code q of the block absmax:
  *     ĉ_b = fl32(q_b · step_g).
  *   - scale2: ceil(n/16384) fp32 values, step_g = fl32(max c1 in g / 255).
- *   - Dequantized weight ŵ_i = fl32(V[k_i] · ĉ_b) with V the 16-value NF4
- *     codebook (qlora_codebook); the linear layer uses RNE_bf16(ŵ_i).
+ *   - Dequantized weight ŵ_i = fl32(V[k_i] · ĉ_b) with V the 16-value table
+ *     of the view's fmt, NF4 by default (qlora_codebook); the linear layer
+ *     uses RNE_bf16(ŵ_i).
  *   - bf16 tensors are raw bfloat16 bit patterns (uint16_t), row-major,
  *     contiguous.
  *
@@ -85,14 +86,27 @@ typedef enum {
 
 typedef uint16_t qlora_bf16; /* raw bfloat16 bits */
 
+/* The 16-entry table the 4-bit codes index.  NF4 is the method's format
+ * (QLoRA-074 §二); the others are the comparison formats of QLoRA-074 §四
+ * (Table 2), run through the same kernels (see qlora_codebook). */
+typedef enum {
+  QLORA_FMT_NF4 = 0,
+  QLORA_FMT_INT4 = 1,
+  QLORA_FMT_FP4_E2M1 = 2,
+  QLORA_FMT_FP4_E3M0 = 3
+} qlora_fmt;
+
 /* Non-owning view of a quantized tensor (QLoRA-074 §三: the frozen W4 codes
  * plus the 8-bit first-level and fp32 second-level constants).  All three
- * buffers are device memory sized by qlora_quant_sizes(n). */
+ * buffers are device memory sized by qlora_quant_sizes(n).  fmt selects the
+ * table of the codes (0 = NF4, so a zero-initialised view is NF4); an
+ * unknown fmt makes every entry point return QLORA_E_INVALID. */
 typedef struct qlora_nf4dq {
   uint8_t* codes;   /* 4*ceil(n/8) bytes      */
   uint8_t* scale8;  /* ceil(n/64) bytes       */
   float* scale2;    /* ceil(n/16384) floats   */
   int64_t n;        /* number of weights      */
+  int32_t fmt;      /* a qlora_fmt            */
 } qlora_nf4dq;
 
 /* ---------------------------------------------------------------- host helpers */
@@ -103,11 +117,17 @@ typedef struct qlora_nf4dq {
 int qlora_quant_sizes(int64_t n, int64_t* codes_bytes, int64_t* scale8_bytes,
                       int64_t* scale2_bytes);
 
-/* The 16 NF4 values as fp32, ascending, generated on the host at load time
- * from normal quantiles (QLoRA-074 §二): 8 positive values
- * Φ⁻¹(1/2 + j(p−1/2)/8), 7 negative −Φ⁻¹(1/2 + j(p−1/2)/7), and 0, all over
- * Φ⁻¹(p), p = 1 − (1/32 + 1/30)/2.  `out` is host memory for 16 floats. */
-int qlora_codebook(float* out);
+/* The 16 values of table `fmt` as fp32, ascending; `out` is host memory for
+ * 16 floats.  QLORA_FMT_NF4 is generated on the host at load time from
+ * normal quantiles (QLoRA-074 §二): 8 positive values Φ⁻¹(1/2 + j(p−1/2)/8),
+ * 7 negative −Φ⁻¹(1/2 + j(p−1/2)/7), and 0, all over Φ⁻¹(p),
+ * p = 1 − (1/32 + 1/30)/2.  The comparison tables (readings of the format
+ * names of QLoRA-074 §四; the pages give no tables): INT4 = (i−8)/7 (the
+ * absmax maps to 7, −8/7 is never nearest); FP4_E2M1 = sign, 2 exponent
+ * bits (bias 1, subnormals), 1 mantissa bit, over 6; FP4_E3M0 = sign and 3
+ * exponent bits, field 0 = zero, field e = 2^(e−7).  Both FP4 tables keep −0
+ * (index 7) and +0 (index 8). */
+int qlora_codebook(int fmt, float* out);
 
 /* Workspace in bytes needed by qlora_linear_fwd (op = QLORA_OP_FWD) or
  * qlora_linear_bwd (op = QLORA_OP_BWD) for these sizes.  Returns 0 for
@@ -129,10 +149,13 @@ const char* qlora_version(void);
  *   d_flags device int32 or NULL.  If any weight is NaN or ±Inf, bit 0 is set
  *          (the word is never cleared by the library; zero it first).  The
  *          outputs of a group holding a non-finite weight are unspecified.
- * Per block: c1 = max |w|; each weight gets the index of the codebook value
- * nearest to w/c1 (exact comparison, ties to the lower index); a zero block
- * gets code 7.  Per group: step = fl32(max c1 / 255); q = the integer in
- * 0..255 nearest to c1/step (ties to the lower), 0 if step is 0. */
+ * Per block: c1 = max |w|; each weight gets the number of table midpoints
+ * strictly below w/c1 (exact comparison): the nearest value, ties to the
+ * lower index (with the duplicated zero of the FP4 tables a weight rounding
+ * to zero keeps its sign, +0 only for w > 0); a zero block gets code 7.
+ * The table is out->fmt; codes past n are 7 for every table.  Per group:
+ * step = fl32(max c1 / 255); q = the integer in 0..255 nearest to c1/step
+ * (ties to the lower), 0 if step is 0. */
 int qlora_quantize_nf4_dq(const float* W, int64_t n, const qlora_nf4dq* out,
                           int32_t* d_flags, void* stream);
 

@@ -22,6 +22,8 @@ LIB_PATH = os.path.join(_PKG, "libqlora.so")
 QLORA_OK, QLORA_E_NONFINITE = 0, 7
 QLORA_F32, QLORA_BF16 = 0, 1
 QLORA_OP_FWD, QLORA_OP_BWD = 0, 1
+# Tables of the 4-bit codes (qlora_fmt).
+FORMATS = {"nf4": 0, "int4": 1, "fp4_e2m1": 2, "fp4_e3m0": 3}
 
 _lib = None
 
@@ -34,7 +36,7 @@ class QloraError(RuntimeError):
 
 class _NF4DQ(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("scale8", ctypes.c_void_p),
-                ("scale2", ctypes.c_void_p), ("n", ctypes.c_int64)]
+                ("scale2", ctypes.c_void_p), ("n", ctypes.c_int64), ("fmt", ctypes.c_int32)]
 
 
 def lib() -> ctypes.CDLL:
@@ -49,7 +51,7 @@ def lib() -> ctypes.CDLL:
     i64, vp, sz, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
     P = ctypes.POINTER
     L.qlora_quant_sizes.argtypes = [i64, P(i64), P(i64), P(i64)]
-    L.qlora_codebook.argtypes = [P(ctypes.c_float)]
+    L.qlora_codebook.argtypes = [i32, P(ctypes.c_float)]
     L.qlora_workspace_bytes.argtypes = [i32, i64, i64, i64, i64]
     L.qlora_workspace_bytes.restype = sz
     L.qlora_strerror.argtypes = [i32]
@@ -89,9 +91,18 @@ def qlora_quant_sizes(n: int) -> tuple[int, int, int]:
     return c.value, s8.value, s2.value
 
 
-def qlora_codebook() -> list[float]:
+def _fmt_code(fmt) -> int:
+    if isinstance(fmt, str):
+        if fmt not in FORMATS:
+            raise ValueError(f"unknown 4-bit format {fmt!r}; one of {sorted(FORMATS)}")
+        return FORMATS[fmt]
+    return int(fmt)
+
+
+def qlora_codebook(fmt="nf4") -> list[float]:
+    """The 16 ascending values of a code table ("nf4", "int4", "fp4_e2m1", "fp4_e3m0")."""
     buf = (ctypes.c_float * 16)()
-    _check(lib().qlora_codebook(buf), "qlora_codebook")
+    _check(lib().qlora_codebook(_fmt_code(fmt), buf), "qlora_codebook")
     return list(buf)
 
 
@@ -161,36 +172,39 @@ class QuantizedWeight:
     scale2: object
     n: int
     shape: tuple
+    fmt: int = 0
 
     def view(self) -> _NF4DQ:
-        return _NF4DQ(self.codes.data_ptr(), self.scale8.data_ptr(), self.scale2.data_ptr(), self.n)
+        return _NF4DQ(self.codes.data_ptr(), self.scale8.data_ptr(), self.scale2.data_ptr(), self.n,
+                      self.fmt)
 
     @property
     def device(self):
         return self.codes.device
 
 
-def _alloc_quantized(n: int, shape, device) -> QuantizedWeight:
+def _alloc_quantized(n: int, shape, device, fmt: int) -> QuantizedWeight:
     torch = _torch()
     c, s8, s2 = qlora_quant_sizes(n)
     return QuantizedWeight(torch.empty(max(c, 1), dtype=torch.uint8, device=device),
                            torch.empty(max(s8, 1), dtype=torch.uint8, device=device),
                            torch.empty(max(s2 // 4, 1), dtype=torch.float32, device=device),
-                           n, tuple(shape))
+                           n, tuple(shape), fmt)
 
 
-def qlora_quantize_nf4_dq(W, check_finite: bool = True, out: QuantizedWeight | None = None
-                          ) -> QuantizedWeight:
-    """Blockwise NF4 + double quantization of an fp32 device tensor (any shape, flattened).
+def qlora_quantize_nf4_dq(W, check_finite: bool = True, out: QuantizedWeight | None = None,
+                          fmt="nf4") -> QuantizedWeight:
+    """Blockwise 4-bit + double quantization of an fp32 device tensor (any shape, flattened).
 
-    `out` reuses the buffers of an earlier result of the same size.  With
+    `fmt` picks the code table (NF4 by default).  `out` reuses the buffers of
+    an earlier result of the same size (and keeps its table).  With
     check_finite the call waits for the kernel and raises on NaN/Inf input.
     """
     torch = _torch()
     _need(W, torch.float32, "W")
     if out is not None and out.n != W.numel():
         raise ValueError("out holds a different number of weights")
-    q = _alloc_quantized(W.numel(), W.shape, W.device) if out is None else out
+    q = _alloc_quantized(W.numel(), W.shape, W.device, _fmt_code(fmt)) if out is None else out
     flags = getattr(q, "flags", None)
     if flags is None:
         flags = torch.zeros(1, dtype=torch.int32, device=W.device)

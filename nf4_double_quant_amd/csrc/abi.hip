@@ -114,6 +114,7 @@ hipError_t timed(int cls, hipStream_t st, F&& f) {
 int check_quant_view(const qlora_nf4dq* q) {
   if (q == nullptr) return QLORA_E_INVALID;
   if (q->n < 0) return QLORA_E_INVALID;
+  if (q->fmt < QLORA_FMT_NF4 || q->fmt > QLORA_FMT_FP4_E3M0) return QLORA_E_INVALID;
   if (q->n > 0 && (q->codes == nullptr || q->scale8 == nullptr || q->scale2 == nullptr))
     return QLORA_E_INVALID;
   if (!aligned16(q->codes) || !aligned16(q->scale8) || !aligned16(q->scale2)) return QLORA_E_ALIGN;
@@ -146,9 +147,9 @@ int qlora_quant_sizes(int64_t n, int64_t* codes_bytes, int64_t* scale8_bytes, in
   return QLORA_OK;
 }
 
-int qlora_codebook(float* out) {
-  if (out == nullptr) return QLORA_E_INVALID;
-  memcpy(out, host_codebook().v, sizeof(float) * 16);
+int qlora_codebook(int fmt, float* out) {
+  if (out == nullptr || fmt < QLORA_FMT_NF4 || fmt > QLORA_FMT_FP4_E3M0) return QLORA_E_INVALID;
+  memcpy(out, host_codebook(fmt).v, sizeof(float) * 16);
   return QLORA_OK;
 }
 
@@ -211,7 +212,8 @@ int qlora_quantize_nf4_dq(const float* W, int64_t n, const qlora_nf4dq* out, int
   if (!aligned16(W)) return QLORA_E_ALIGN;
   if (n == 0) return QLORA_OK;
   if ((st = device_status())) return st;
-  QL_RUN(QLORA_K_QUANTIZE, (hipStream_t)stream, launch_quantize(W, n, out->codes, out->scale8, out->scale2, d_flags, (hipStream_t)stream));
+  QL_RUN(QLORA_K_QUANTIZE, (hipStream_t)stream, launch_quantize(W, n, out->codes, out->scale8, out->scale2, d_flags,
+                                                                   host_codebook(out->fmt), (hipStream_t)stream));
   return QLORA_OK;
 }
 
@@ -224,7 +226,7 @@ int qlora_dequant(const qlora_nf4dq* q, int out_dtype, void* out, void* stream) 
   if (q->n == 0) return QLORA_OK;
   if ((st = device_status())) return st;
   QL_RUN(QLORA_K_DEQUANT, (hipStream_t)stream, launch_dequant(q->codes, q->scale8, q->scale2, q->n, out_dtype == QLORA_BF16, out,
-                        (hipStream_t)stream));
+                        host_codebook(q->fmt), (hipStream_t)stream));
   return QLORA_OK;
 }
 
@@ -251,7 +253,7 @@ int qlora_linear_fwd(const qlora_bf16* X, int64_t M, int64_t d, const qlora_nf4d
   if (L.gemv) {
     QL_RUN(QLORA_K_GEMV, hs,
            launch_gemv_fwd(X, (int)M, d, W->codes, W->scale8, W->scale2, o, A, B, (int)r, s, Y,
-                           T_out, Tpart, hs));
+                           T_out, Tpart, host_codebook(W->fmt), hs));
     return QLORA_OK;
   }
   uint16_t* sT = reinterpret_cast<uint16_t*>(w + L.sT);
@@ -264,7 +266,7 @@ int qlora_linear_fwd(const qlora_bf16* X, int64_t M, int64_t d, const qlora_nf4d
   }
   QL_RUN(QLORA_K_MAIN_GEMM, hs,
          launch_qgemm(false, X, d, W->codes, W->scale8, W->scale2, d, sT, r, B, o, M, o, d,
-                      lora ? r : 0, Y, o, hs));
+                      lora ? r : 0, Y, o, host_codebook(W->fmt), hs));
   return QLORA_OK;
 }
 
@@ -329,7 +331,7 @@ int qlora_linear_bwd(const qlora_bf16* dY, const qlora_bf16* X, const float* T, 
   if (dX != nullptr) {
     QL_RUN(QLORA_K_MAIN_GEMM, hs,
            launch_qgemm(true, dY, o, W->codes, W->scale8, W->scale2, d, sU, r, A, r, M, d, o,
-                        lora ? r : 0, dX, d, hs));
+                        lora ? r : 0, dX, d, host_codebook(W->fmt), hs));
   }
   return QLORA_OK;
 }

@@ -9,6 +9,13 @@
 // double and rounded to fp32 once.
 //
 // Φ⁻¹ here is Newton's method on Φ(x) = erfc(−x/√2)/2 in long double.
+//
+// The comparison tables of QLoRA-074 §四 (Table 2) go through the same
+// kernels as other 16-entry tables in [-1, 1] (readings; the pages give no
+// tables): int4 = (i − 8)/7 (absmax maps to 7; −8/7 is never nearest);
+// FP4 E2M1 = sign, 2 exponent bits (bias 1, with subnormals), 1 mantissa
+// bit, over 6; FP4 E3M0 = sign and 3 exponent bits, field 0 = zero, field e
+// = 2^(e−7).  Both FP4 tables keep −0 and +0.
 #include <cmath>
 
 #include "common.h"
@@ -35,7 +42,14 @@ double normal_quantile(double p) {
   return (double)x;
 }
 
-Codebook build() {
+Codebook finish(const double (&vals)[16]) {
+  Codebook cb;
+  for (int i = 0; i < 16; ++i) cb.v[i] = (float)vals[i];
+  for (int i = 0; i < 15; ++i) cb.mid[i] = ((double)cb.v[i] + (double)cb.v[i + 1]) * 0.5;
+  return cb;
+}
+
+Codebook build_nf4() {
   const double p_max = 1.0 - 0.5 * (1.0 / 32.0 + 1.0 / 30.0);
   const double half_span = p_max - 0.5;
   const double z_max = normal_quantile(p_max);
@@ -46,17 +60,44 @@ Codebook build() {
   vals[k++] = 0.0;
   for (int j = 1; j <= 8; ++j)
     vals[k++] = normal_quantile(0.5 + half_span * ((double)j / 8.0)) / z_max;
-  Codebook cb;
-  for (int i = 0; i < 16; ++i) cb.v[i] = (float)vals[i];
-  for (int i = 0; i < 15; ++i) cb.mid[i] = ((double)cb.v[i] + (double)cb.v[i + 1]) * 0.5;
-  return cb;
+  return finish(vals);
+}
+
+Codebook build_int4() {
+  double vals[16];
+  for (int i = 0; i < 16; ++i) vals[i] = (double)(i - 8) / 7.0;
+  return finish(vals);
+}
+
+// Ascending table of a 4-bit sign-magnitude format from the magnitudes of
+// its 8 positive codes (ascending, starting at 0): −m7 .. −m1, −0, +0, m1 .. m7.
+Codebook build_signed(const double (&mag)[8], double scale) {
+  double vals[16];
+  for (int i = 0; i < 8; ++i) vals[i] = -mag[7 - i] / scale;   // vals[7] = −0
+  for (int i = 0; i < 8; ++i) vals[8 + i] = mag[i] / scale;
+  return finish(vals);
+}
+
+Codebook build_e2m1() {
+  double mag[8];
+  for (int c = 0; c < 8; ++c) {
+    const int e = c >> 1, m = c & 1;
+    mag[c] = e == 0 ? 0.5 * m : std::ldexp(1.0 + 0.5 * m, e - 1);
+  }
+  return build_signed(mag, 6.0);
+}
+
+Codebook build_e3m0() {
+  double mag[8];
+  for (int e = 0; e < 8; ++e) mag[e] = e == 0 ? 0.0 : std::ldexp(1.0, e - 7);
+  return build_signed(mag, 1.0);
 }
 
 }  // namespace
 
-const Codebook& host_codebook() {
-  static const Codebook cb = build();
-  return cb;
+const Codebook& host_codebook(int fmt) {
+  static const Codebook tables[4] = {build_nf4(), build_int4(), build_e2m1(), build_e3m0()};
+  return tables[fmt >= 0 && fmt < 4 ? fmt : 0];
 }
 
 }  // namespace qlora

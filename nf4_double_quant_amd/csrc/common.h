@@ -24,8 +24,9 @@ struct Codebook {
   double mid[15];
 };
 
-// Host-side codebook, built once when the library loads.
-const Codebook& host_codebook();
+// Host-side 16-entry tables, built once when the library loads: 0 = NF4,
+// 1 = int4, 2 = FP4 E2M1, 3 = FP4 E3M0 (the qlora_fmt values).
+const Codebook& host_codebook(int fmt = 0);
 
 __device__ __forceinline__ uint16_t bf16_bits(float x) {
   // gfx950 converts with round-to-nearest-even (v_cvt_pk_bf16_f32).

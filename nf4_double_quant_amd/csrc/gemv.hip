@@ -308,7 +308,7 @@ int gemv_tsplits(int64_t d) { return (int)((d + kPrepK - 1) / kPrepK); }
 hipError_t launch_gemv_fwd(const uint16_t* X, int M, int64_t d, const uint8_t* codes,
                            const uint8_t* scale8, const float* scale2, int64_t o,
                            const uint16_t* A, const uint16_t* B, int r, float s, uint16_t* Y,
-                           float* T_out, float* Tpart, hipStream_t st) {
+                           float* T_out, float* Tpart, const Codebook& cb, hipStream_t st) {
   const int ts = gemv_tsplits(d);
   const int rr = (r > 0 && (s != 0.0f || T_out != nullptr)) ? r : 0;
   if (rr > 0) {
@@ -317,7 +317,7 @@ hipError_t launch_gemv_fwd(const uint16_t* X, int M, int64_t d, const uint8_t* c
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  GemvArgs p{X, codes, scale8, scale2, Tpart, B, Y, T_out, d, o, M, rr, ts, s, host_codebook()};
+  GemvArgs p{X, codes, scale8, scale2, Tpart, B, Y, T_out, d, o, M, rr, ts, s, cb};
   const unsigned grid = (unsigned)((o + 15) / 16);
   // enough waves to keep every CU streaming: split the reduction 4 ways
   // when there are many row groups, 8 ways otherwise

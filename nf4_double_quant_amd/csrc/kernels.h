@@ -7,10 +7,11 @@
 namespace qlora {
 
 
+// cb: the 16-entry table of the codes (host_codebook(fmt)).
 hipError_t launch_quantize(const float* W, int64_t n, uint8_t* codes, uint8_t* scale8,
-                           float* scale2, int32_t* flags, hipStream_t st);
+                           float* scale2, int32_t* flags, const Codebook& cb, hipStream_t st);
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scale8, const float* scale2,
-                          int64_t n, bool bf16, void* out, hipStream_t st);
+                          int64_t n, bool bf16, void* out, const Codebook& cb, hipStream_t st);
 
 
 // Fused NF4 dequant-GEMM: C = A·Ŵ (+ A2·B2) with Ŵ from the quantized Wq[o][d].
@@ -20,7 +21,7 @@ hipError_t launch_qgemm(bool trans_w, const uint16_t* A, int64_t lda, const uint
                         const uint8_t* scale8, const float* scale2, int64_t d,
                         const uint16_t* A2, int64_t lda2, const uint16_t* B2, int64_t ldb2,
                         int64_t M, int64_t N, int64_t K, int64_t K2, uint16_t* C, int64_t ldc,
-                        hipStream_t st);
+                        const Codebook& cb, hipStream_t st);
 
 // Rank-r products (split planes, summed by launch_reduce_planes):
 // part[z][M][r] = P[M][K-slice z]·Q with Q = Qsrc[K][r], or Q = Qsrc[r][K]ᵀ
@@ -50,6 +51,6 @@ int gemv_tsplits(int64_t d);
 hipError_t launch_gemv_fwd(const uint16_t* X, int M, int64_t d, const uint8_t* codes,
                            const uint8_t* scale8, const float* scale2, int64_t o,
                            const uint16_t* A, const uint16_t* B, int r, float s, uint16_t* Y,
-                           float* T_out, float* Tpart, hipStream_t st);
+                           float* T_out, float* Tpart, const Codebook& cb, hipStream_t st);
 
 }  // namespace qlora

@@ -445,10 +445,10 @@ hipError_t launch_qgemm(bool trans_w, const uint16_t* A, int64_t lda, const uint
                         const uint8_t* scale8, const float* scale2, int64_t d,
                         const uint16_t* A2, int64_t lda2, const uint16_t* B2, int64_t ldb2,
                         int64_t M, int64_t N, int64_t K, int64_t K2, uint16_t* C, int64_t ldc,
-                        hipStream_t st) {
+                        const Codebook& cb, hipStream_t st) {
   if (M == 0 || N == 0) return hipSuccess;
   QGemmArgs p{A, lda, codes, scale8, scale2, d, A2, lda2, B2, ldb2, M, N, K, K2, C, ldc,
-              host_codebook()};
+              cb};
   const unsigned tiles = (unsigned)(((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN));
   if (trans_w)
     hipLaunchKernelGGL((k_qgemm<true, kWaves>), dim3(tiles), dim3(64 * kWaves), 0, st, p);

@@ -170,8 +170,22 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, i
   const int64_t code_bytes = (n + 7) / 8 * 4;
   const int64_t cbase = g * (kGroupElems / 2);
   const Rsrc rcod = rsrc(codes + cbase, code_bytes - cbase);
-  const uint4 a = reinterpret_cast<const uint4*>(s_codes)[t * 2];
-  const uint4 b = reinterpret_cast<const uint4*>(s_codes)[t * 2 + 1];
+  uint4 a = reinterpret_cast<const uint4*>(s_codes)[t * 2];
+  uint4 b = reinterpret_cast<const uint4*>(s_codes)[t * 2 + 1];
+  // The word holding code n-1 may end in codes past n; they are stored as 7,
+  // the layout's padding, whatever a zero weight encodes to in this table.
+  const int64_t nvalid = n - base;
+  if (nvalid < kGroupElems && (nvalid & 7) != 0 && (nvalid >> 6) == t) {
+    uint32_t keep = 0;
+    for (int j = 0; j < (int)(nvalid & 7); ++j) keep |= 0xFu << (8 * (j & 3) + 4 * (j >> 2));
+    const int wi = (int)((nvalid >> 3) & 7);
+    uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (k == wi) w[k] = (w[k] & keep) | (0x77777777u & ~keep);
+    a = make_uint4(w[0], w[1], w[2], w[3]);
+    b = make_uint4(w[4], w[5], w[6], w[7]);
+  }
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) int, a), rcod, t * 32, 0, 0);
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) int, b), rcod, t * 32 + 16, 0, 0);
   if (bad && flags != nullptr) flags[0] = flags[0] | 1;
@@ -230,26 +244,26 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ cod
 
 // ------------------------------------------------------------------ launchers
 hipError_t launch_quantize(const float* W, int64_t n, uint8_t* codes, uint8_t* scale8,
-                           float* scale2, int32_t* flags, hipStream_t st) {
+                           float* scale2, int32_t* flags, const Codebook& cb, hipStream_t st) {
   const int64_t ng = (n + kGroupElems - 1) / kGroupElems;
   if (ng == 0) return hipSuccess;
   hipLaunchKernelGGL(k_quantize, dim3((unsigned)ng), dim3(256), 0, st, W, n, codes, scale8,
-                     scale2, flags, host_codebook());
+                     scale2, flags, cb);
   return hipGetLastError();
 }
 
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scale8, const float* scale2,
-                          int64_t n, bool bf16, void* out, hipStream_t st) {
+                          int64_t n, bool bf16, void* out, const Codebook& cb, hipStream_t st) {
   const int64_t n8 = (n + 7) / 8;
   if (n8 == 0) return hipSuccess;
   int64_t blocks = (n8 + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   if (bf16)
     hipLaunchKernelGGL(k_dequant<true>, dim3((unsigned)blocks), dim3(256), 0, st, codes, scale8,
-                       scale2, n, out, host_codebook());
+                       scale2, n, out, cb);
   else
     hipLaunchKernelGGL(k_dequant<false>, dim3((unsigned)blocks), dim3(256), 0, st, codes, scale8,
-                       scale2, n, out, host_codebook());
+                       scale2, n, out, cb);
   return hipGetLastError();
 }
 

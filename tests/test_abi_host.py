@@ -16,7 +16,7 @@ import re
 import numpy as np
 import pytest
 
-from oracle import nf4
+from oracle import formats, nf4
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "qlora.h")
@@ -58,6 +58,21 @@ def test_library_codebook_equals_oracle(L):
     assert lib_v.tobytes() == nf4.codebook().tobytes()
 
 
+@pytest.mark.parametrize("fmt", formats.FORMATS)
+def test_library_tables_equal_oracle(L, fmt):
+    """Every code table, −0 and +0 included, equals the oracle's bit for bit."""
+    lib_v = np.array(qb.qlora_codebook(fmt), dtype=np.float32)
+    assert lib_v.tobytes() == formats.codebook(fmt).tobytes()
+    assert qb.qlora_codebook(qb.FORMATS[fmt]) == list(lib_v)
+
+
+def test_unknown_table_is_rejected(L):
+    buf = (ctypes.c_float * 16)()
+    for bad in (-1, 4, 99):
+        assert L.qlora_codebook(bad, buf) == 1
+    assert L.qlora_codebook(0, None) == 1
+
+
 def test_workspace_and_strings(L):
     # the fused dequant-GEMM never stages a dequantized weight in the
     # workspace: it holds only rank-r planes, independent of o·d at fixed d, o
@@ -81,8 +96,8 @@ def test_workspace_and_strings(L):
 A16 = 0x10000
 
 
-def _view(n, codes=A16, s8=A16, s2=A16):
-    return qb._NF4DQ(codes, s8, s2, n)
+def _view(n, codes=A16, s8=A16, s2=A16, fmt=0):
+    return qb._NF4DQ(codes, s8, s2, n, fmt)
 
 
 def test_validation_statuses(L):
@@ -109,12 +124,16 @@ def test_validation_statuses(L):
     assert call(wsb=16) == 4                                # workspace
     assert call(A=None) == 1                                # adapters required for r > 0
     assert call(M=-1) == 2
+    for bad in (-1, 4):                                     # unknown code table
+        assert call(view=_view(128 * 128, fmt=bad)) == 1
     # quantize / dequant
     q = L.qlora_quantize_nf4_dq
     assert q(A16, -5, ctypes.byref(_view(0)), None, None) == 1
     assert q(A16, 100, ctypes.byref(_view(99)), None, None) == 2
     assert q(A16 + 8, 100, ctypes.byref(_view(100)), None, None) == 3
     assert L.qlora_dequant(ctypes.byref(_view(100)), 5, A16, None) == 1
+    assert q(A16, 100, ctypes.byref(_view(100, fmt=7)), None, None) == 1
+    assert L.qlora_dequant(ctypes.byref(_view(100, fmt=-2)), 0, A16, None) == 1
     # bwd
     bwd = L.qlora_linear_bwd
     assert bwd(A16, A16, None, 8, 128, ctypes.byref(v), 128, A16, A16, 8, 2.0, A16, None, A16,
