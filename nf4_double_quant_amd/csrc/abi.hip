@@ -29,7 +29,7 @@ FwdLayout fwd_layout(int64_t M, int64_t d, int64_t o, int64_t r) {
   (void)o;
   FwdLayout L{};
   int64_t off = 0;
-  L.gemv = M <= kGemvMaxTokens;
+  L.gemv = M <= kGemvMaxTokens && gemv_fits(M, d, r);
   L.t_splits = L.gemv ? gemv_tsplits(d) : rank_down_splits(d);
   L.Tpart = off; off += up(4 * L.t_splits * M * r);
   if (!L.gemv) {

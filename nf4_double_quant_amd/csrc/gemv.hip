@@ -24,6 +24,8 @@
 // the activations as the A operand straight from memory and A's columns as
 // the B operand, read from a row-major LDS tile with ds_read_b64_tr_b16
 // (each 16-lane group gathers 4 consecutive k of 16 columns).
+#include <algorithm>
+
 #include "kernels.h"
 
 namespace qlora {
@@ -47,6 +49,16 @@ __global__ __launch_bounds__(256) void k_lora_down_small(const uint16_t* __restr
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int64_t k0 = (int64_t)blockIdx.x * kPrepK;
   const int c0 = blockIdx.y * 64;
+  const int m = lane & 15, g = lane >> 4, s = lane & 15;
+  // this lane's activations for its four 32-wide k steps, requested before
+  // the adapter tile so that both arrive in one round trip
+  uint4 xv[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t kx = k0 + (w * 4 + q) * 32 + 8 * g;
+    xv[q] = make_uint4(0, 0, 0, 0);
+    if (m < M && kx < d) xv[q] = *reinterpret_cast<const uint4*>(X + (int64_t)m * d + kx);
+  }
   // stage A[k0:k0+512][c0:c0+64] (zeros outside); all 16 loads of a thread
   // are in flight before the first store
   {
@@ -69,14 +81,10 @@ __global__ __launch_bounds__(256) void k_lora_down_small(const uint16_t* __restr
   f32x4 acc[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  const int m = lane & 15, g = lane >> 4, s = lane & 15;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int kq = w * 4 + q;                    // 32-wide k step inside the slice
-    const int64_t kx = k0 + kq * 32 + 8 * g;
-    uint4 xv = make_uint4(0, 0, 0, 0);
-    if (m < M && kx < d) xv = *reinterpret_cast<const uint4*>(X + (int64_t)m * d + kx);
-    const bf16x8 a = __builtin_bit_cast(bf16x8, xv);
+    const bf16x8 a = __builtin_bit_cast(bf16x8, xv[q]);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int row = kq * 32 + 8 * g + (s >> 2);
@@ -104,6 +112,9 @@ __global__ __launch_bounds__(256) void k_lora_down_small(const uint16_t* __restr
   }
 }
 
+constexpr int kGemvMaxWaves = 12;
+constexpr int kGemvMaxLds = 65536;
+
 struct GemvArgs {
   const uint16_t* X;    // [M][d]
   const uint8_t* codes; const uint8_t* scale8; const float* scale2;
@@ -113,6 +124,7 @@ struct GemvArgs {
   float* T_out;         // [M][r] or null
   int64_t d, o;
   int M, r, tsplits;
+  int t_regs;           // 1: T planes fit the register path (host-checked LDS size)
   float s;
   Codebook cb;
 };
@@ -172,79 +184,255 @@ __device__ __forceinline__ uint4 gload16(GRsrc r, uint32_t off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
 
-// One 4-block group of a wave: lane (n = lane%16, q = lane/16) holds block
-// 4·g + q of row n — 64 codes, its 8-bit scale and its group step.
+// One 4-block group of a wave: lane (n = lane%16, q = lane/16) holds the 64
+// codes of one block of row n.
 struct GemvCodes {
   uint4 c0, c1;
-  uint32_t q8;
+  uint32_t q8;          // the dword of scale8 holding the block's byte
   float step;
 };
 
-template <int WAVES>
-__global__ __launch_bounds__(WAVES * 64) void k_gemv(GemvArgs p) {
-  __shared__ float s_part[WAVES][16][17];
-  __shared__ float s_T[16 * kMaxGemvRank];
-  __shared__ float s_B[kMaxGemvRank * 16];
+// Shared-memory layout of k_gemv, computed identically on host and device.
+struct GemvSmem {
+  int x, part, tp, t, b, bytes;   // byte offsets of each region, total size
+};
+__host__ __device__ inline GemvSmem gemv_smem(int nw, int mx, int M, int r, int tplanes,
+                                              bool t_regs) {
+  GemvSmem s;
+  int off = 0;
+  s.x = off;    off += mx <= 4 ? nw * (mx + 1) * 36 * 16 : 0; // staged activations + a zero row
+  s.part = off; off += nw * 16 * 17 * 4;                      // per-wave partial sums
+  s.tp = off;   off += t_regs ? tplanes * M * r * 4 : 0;      // T planes (register path)
+  s.t = off;    off += M * r * 4;                             // T = X·A
+  s.b = off;    off += r * 16 * 4;                            // B[:, n0:n0+16]
+  s.bytes = off;
+  return s;
+}
+
+// The waves of a workgroup share its 16 rows and split the reduction in
+// 256-weight groups (4 blocks): wave w takes groups w, w + nw, ....  The
+// host picks nw = ceil(groups / 4) up to kGemvMaxWaves, so for d <= 12288
+// every wave owns at most four groups and issues all its loads at once.
+//
+// MX (the largest M the instance serves) selects how the activations reach
+// the MFMA A operand.  The operand lane (m, q) needs the 128 bytes of row m
+// under its block.  For MX <= 4 the wave loads the group's M×512 bytes with
+// ceil(M/2) 16-byte loads and redistributes them through a wave-private LDS
+// tile; for larger M every operand lane loads its 128 bytes itself.
+template <int MX>
+__global__ __launch_bounds__(kGemvMaxWaves * 64) void k_gemv(GemvArgs p) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  constexpr bool kStage = MX <= 4;
+  constexpr int kNX = kStage ? (MX * 32 + 63) / 64 : 8;     // activation loads per lane per group
+  constexpr int kXRow = 36;                                 // staged row: 4 blocks × (8 + 1 pad) uint4
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int nw = (int)(blockDim.x >> 6), nthr = (int)blockDim.x;
   const int64_t n0 = (int64_t)blockIdx.x * 16;
   const uint32_t nblk = (uint32_t)(p.d / kBlock);
   const uint32_t ngrp = (nblk + 3) / 4;
   const int nl = lane & 15, q = lane >> 4, m = lane & 15;
   const int64_t n = n0 + nl;
   const bool lora = p.r > 0 && p.s != 0.0f;
+  const bool want_t = lora || (p.T_out != nullptr && blockIdx.x == 0);
+  const int tpl = p.tsplits * p.M * p.r;                    // T-plane elements
+  const bool t_regs = want_t && p.t_regs != 0;
+  const bool b_regs = lora && p.r * 8 <= 2 * nthr;
+  const GemvSmem L = gemv_smem(nw, MX, p.M, p.r, p.tsplits, p.t_regs != 0);
+  float* s_part = reinterpret_cast<float*>(smem + L.part);  // [nw][16][17]
+  float* s_tp = reinterpret_cast<float*>(smem + L.tp);      // [tsplits][M][r]
+  float* s_T = reinterpret_cast<float*>(smem + L.t);        // [M][r]
+  float* s_B = reinterpret_cast<float*>(smem + L.b);        // [r][16]
+  uint4* s_x = reinterpret_cast<uint4*>(smem + L.x) + w * ((MX + 1) * kXRow);
 
-  // ---- weight stream.  Every offset is 32-bit (the host bounds the weight
-  // count); rows past o and blocks past the row end read 0 (a zero table
-  // and zero activations contribute nothing).
-  const uint32_t nbt = (uint32_t)(p.o * nblk);            // blocks in Wq
+  // ---- every global load is unconditional (offsets past a buffer read 0),
+  // so the wait before each use counts exactly the loads issued after it.
+  // Offsets are 32-bit (the host bounds the sizes); rows past o and blocks
+  // past the row end read 0 (a zero table and zero activations contribute
+  // nothing).
+  const uint32_t nbt = (uint32_t)(p.o * nblk);            // blocks in Wq (a multiple of 8)
   const GRsrc rc = grsrc(p.codes, (int64_t)nbt * 32);
   const GRsrc rs8 = grsrc(p.scale8, nbt);
   const GRsrc rs2 = grsrc(p.scale2, (int64_t)((nbt + kGroup - 1) / kGroup) * 4);
   const GRsrc rx = grsrc(p.X, (int64_t)p.M * p.d * 2);
+  const GRsrc rt = grsrc(p.Tpart, t_regs ? (int64_t)tpl * 4 : 0);
+  const GRsrc rb = grsrc(p.B, lora ? (int64_t)p.r * p.o * 2 : 0);
+
+  // T split-K planes and B[:, n0:n0+16] for the epilogue, requested before
+  // the weight stream so that no later wait holds it up
+  float tp[4];
+  uint32_t bb[2];
+  if (t_regs) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = t + u * nthr;
+      tp[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                            rt, (int)(e < tpl ? (uint32_t)e * 4 : kGOob), 0, 0));
+    }
+  }
+  if (b_regs) {
+    // dword i: row j = i/8 of B, columns n0 + 2(i%8), +1 (o is a multiple of 8)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = t + u * nthr, j = i >> 3, c2 = i & 7;
+      const bool ok = i < p.r * 8 && n0 + 2 * c2 < p.o;
+      bb[u] = __builtin_amdgcn_raw_buffer_load_b32(
+          rb, (int)(ok ? ((uint32_t)j * (uint32_t)p.o + (uint32_t)n0 + 2 * c2) * 2 : kGOob), 0, 0);
+    }
+  }
+
+  if constexpr (kStage) {
+    if (lane < kXRow) s_x[MX * kXRow + lane] = make_uint4(0, 0, 0, 0);
+  }
   const bool row_ok = n < p.o;
   const uint32_t brow = row_ok ? (uint32_t)n * nblk : 0u;
-  // groups of this wave: g = w, w + WAVES, ...; iterations past the end read 0
-  const int niter = (int)ngrp > w ? ((int)ngrp - w + WAVES - 1) / WAVES : 0;
+  // the 8-bit scale of block b is byte b%4 of dword b/4; b%4 = (brow + q)%4
+  // for every block this lane touches
+  const uint32_t sh8 = ((brow + (uint32_t)q) & 3u) * 8u;
+  const int niter = (int)ngrp > w ? ((int)ngrp - w + nw - 1) / nw : 0;
+  // group of the wave's slot `it`
+  auto group_of = [&](int it) -> uint32_t {
+    return (uint32_t)(w + it * nw);
+  };
   auto load_codes = [&](int it, GemvCodes& c) {
-    const uint32_t kb = (uint32_t)(w + it * WAVES) * 4 + q;
+    const uint32_t kb = group_of(it) * 4 + q;
     const bool ok = row_ok && kb < nblk;
     const uint32_t b = brow + kb;
     c.c0 = gload16(rc, ok ? b * 32 : kGOob);
     c.c1 = gload16(rc, ok ? b * 32 + 16 : kGOob);
-    c.q8 = __builtin_amdgcn_raw_buffer_load_b8(rs8, (int)(ok ? b : kGOob), 0, 0);
+    c.q8 = __builtin_amdgcn_raw_buffer_load_b32(rs8, (int)(ok ? b & ~3u : kGOob), 0, 0);
     c.step = __builtin_bit_cast(
         float, __builtin_amdgcn_raw_buffer_load_b32(rs2, (int)(ok ? (b / kGroup) * 4 : kGOob), 0, 0));
   };
-  auto load_x = [&](int it, uint4 (&x)[8]) {
-    const uint32_t kb = (uint32_t)(w + it * WAVES) * 4 + q;
-    const bool ok = m < p.M && kb < nblk;
-    const uint32_t o0 = ok ? ((uint32_t)m * (uint32_t)p.d + kb * kBlock) * 2 : kGOob;
+  // activations of slot `it`: staged layout (chunk c = u·64 + lane holds
+  // row c/32, 8 values at k = 8·(c%32) of the group) or operand layout
+  auto load_x = [&](int it, uint4 (&x)[kNX]) {
+    const uint32_t g = group_of(it);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) x[j] = gload16(rx, o0 + 16 * j);
+    for (int u = 0; u < kNX; ++u) {
+      uint32_t off;
+      bool ok;
+      if constexpr (kStage) {
+        const int c = u * 64 + lane, mm = c >> 5, kc = c & 31;
+        ok = mm < p.M && g * 4 + (kc >> 3) < nblk;
+        off = ((uint32_t)mm * (uint32_t)p.d + g * 256 + kc * 8) * 2;
+      } else {
+        const uint32_t kb = g * 4 + q;
+        ok = m < p.M && kb < nblk;
+        off = ((uint32_t)m * (uint32_t)p.d + kb * kBlock) * 2 + 16 * u;
+      }
+      x[u] = gload16(rx, ok ? off : kGOob);
+    }
+  };
+  // staged activations -> operand layout, through this wave's LDS tile
+  // (row stride and a pad after every block make the reads conflict-free)
+  auto operands = [&](const uint4 (&x)[kNX], uint4 (&xa)[8]) {
+    if constexpr (kStage) {
+#pragma unroll
+      for (int u = 0; u < kNX; ++u) {
+        const int c = u * 64 + lane, mm = c >> 5, kc = c & 31;
+        if (mm < MX) s_x[mm * kXRow + kc + (kc >> 3)] = x[u];
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // operand rows m >= M read zeros: rows M..MX-1 were staged from
+      // out-of-range loads, and row MX is the zero row
+      const int mr = m < MX ? m : MX;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) xa[j] = s_x[mr * kXRow + q * 9 + j];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) xa[j] = x[j];
+    }
   };
   f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  auto compute = [&](const GemvCodes& c, const uint4 (&x)[8]) {
+  auto compute = [&](const GemvCodes& c, const uint4 (&x)[kNX]) {
+    uint4 xa[8];
+    operands(x, xa);
     Lut lut;
-    build_lut(p.cb, (float)c.q8 * c.step, lut);   // ĉ = fl32(q8·step)
+    const float q8 = (float)__builtin_amdgcn_ubfe(c.q8, sh8, 8);
+    build_lut(p.cb, q8 * c.step, lut);            // ĉ = fl32(q8·step)
     const uint32_t cw[8] = {c.c0.x, c.c0.y, c.c0.z, c.c0.w, c.c1.x, c.c1.y, c.c1.z, c.c1.w};
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x[j]), expand8(lut, cw[j]),
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa[j]), expand8(lut, cw[j]),
                                                     acc, 0, 0, 0);
   };
-  // codes of four groups in flight, activations of two (branch-free: the
-  // steps past niter load and multiply zeros)
+
+  // Four groups of codes in flight; the loop runs while more chunks follow
+  // the one held, and the last four slots are computed after it with no
+  // further loads (slots past niter hold zeros).
   GemvCodes c0, c1, c2, c3;
-  uint4 xa[8], xb[8];
-  load_codes(0, c0); load_codes(1, c1); load_codes(2, c2); load_codes(3, c3);
-  load_x(0, xa);
-  // ---- the adapter pieces the epilogue needs, fetched after the first
-  // weight loads are in flight so their latency overlaps: T (summed over
-  // its split-K planes, fixed order) and B[:, n0:n0+16]
-  if (lora || (p.T_out != nullptr && blockIdx.x == 0)) {
+  if constexpr (kStage) {
+    uint4 x0[kNX], x1[kNX], x2[kNX], x3[kNX];
+    // (the scheduling barriers keep each group's loads together, in order,
+    // so that the wait for a group never covers a later one)
+    load_codes(0, c0); load_x(0, x0); __builtin_amdgcn_sched_barrier(0);
+    load_codes(1, c1); load_x(1, x1); __builtin_amdgcn_sched_barrier(0);
+    load_codes(2, c2); load_x(2, x2); __builtin_amdgcn_sched_barrier(0);
+    load_codes(3, c3); load_x(3, x3); __builtin_amdgcn_sched_barrier(0);
+    int it = 0;
+    for (; it + 4 < niter; it += 4) {
+      compute(c0, x0); load_codes(it + 4, c0); load_x(it + 4, x0); __builtin_amdgcn_sched_barrier(0);
+      compute(c1, x1); load_codes(it + 5, c1); load_x(it + 5, x1); __builtin_amdgcn_sched_barrier(0);
+      compute(c2, x2); load_codes(it + 6, c2); load_x(it + 6, x2); __builtin_amdgcn_sched_barrier(0);
+      compute(c3, x3); load_codes(it + 7, c3); load_x(it + 7, x3); __builtin_amdgcn_sched_barrier(0);
+    }
+    compute(c0, x0);
+    compute(c1, x1);
+    compute(c2, x2);
+    compute(c3, x3);
+  } else {
+    // activations one group ahead
+    uint4 xa[8], xb[8];
+    load_codes(0, c0); __builtin_amdgcn_sched_barrier(0);
+    load_x(0, xa); __builtin_amdgcn_sched_barrier(0);
+    load_codes(1, c1); load_codes(2, c2); load_codes(3, c3); __builtin_amdgcn_sched_barrier(0);
+    int it = 0;
+    for (; it + 4 < niter; it += 4) {
+      load_x(it + 1, xb); compute(c0, xa); load_codes(it + 4, c0);
+      load_x(it + 2, xa); compute(c1, xb); load_codes(it + 5, c1);
+      load_x(it + 3, xb); compute(c2, xa); load_codes(it + 6, c2);
+      load_x(it + 4, xa); compute(c3, xb); load_codes(it + 7, c3);
+    }
+    load_x(it + 1, xb); compute(c0, xa);
+    load_x(it + 2, xa); compute(c1, xb);
+    load_x(it + 3, xb); compute(c2, xa);
+    compute(c3, xb);
+  }
+
+  // ---- epilogue: Y = Σ partials + s·T·B
+  // lane holds rows m = 4*(lane/16) + v of column n = lane%16
+#pragma unroll
+  for (int v = 0; v < 4; ++v) s_part[(w * 16 + 4 * (lane >> 4) + v) * 17 + (lane & 15)] = acc[v];
+  if (t_regs) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = t + u * nthr;
+      if (e < tpl) s_tp[e] = tp[u];
+    }
+  }
+  if (b_regs) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = t + u * nthr;
+      if (i < p.r * 8) {
+        s_B[2 * i] = bf16_to_f32((uint16_t)(bb[u] & 0xFFFFu));
+        s_B[2 * i + 1] = bf16_to_f32((uint16_t)(bb[u] >> 16));
+      }
+    }
+  } else if (lora) {
+    for (int i = t; i < p.r * 16; i += nthr) {
+      const int j = i >> 4, c = i & 15;
+      s_B[i] = n0 + c < p.o ? bf16_to_f32(p.B[(int64_t)j * p.o + n0 + c]) : 0.0f;
+    }
+  }
+  if (want_t && !t_regs) {
     const int64_t plane = (int64_t)p.M * p.r;
-    for (int i = t; i < p.M * p.r; i += WAVES * 64) {
-      // planes summed in order, eight loads in flight at a time
+    for (int i = t; i < p.M * p.r; i += nthr) {
       float sum = 0.0f;
       int z = 0;
       for (; z + 8 <= p.tsplits; z += 8) {
@@ -259,40 +447,24 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(GemvArgs p) {
       if (p.T_out != nullptr && blockIdx.x == 0) p.T_out[i] = sum;
     }
   }
-  if (lora) {
-    for (int i = t; i < p.r * 16; i += WAVES * 64) {
-      const int j = i >> 4, c = i & 15;
-      s_B[i] = n0 + c < p.o ? bf16_to_f32(p.B[(int64_t)j * p.o + n0 + c]) : 0.0f;
-    }
-  }
-
-  for (int it = 0; it < niter; it += 4) {
-    load_x(it + 1, xb);
-    compute(c0, xa);
-    load_codes(it + 4, c0);
-    load_x(it + 2, xa);
-    compute(c1, xb);
-    load_codes(it + 5, c1);
-    if (it + 2 < niter) {
-      load_x(it + 3, xb);
-      compute(c2, xa);
-      load_codes(it + 6, c2);
-      load_x(it + 4, xa);
-      compute(c3, xb);
-      load_codes(it + 7, c3);
-    }
-  }
-  // lane holds rows m = 4*(lane/16) + v of column n = lane%16
-#pragma unroll
-  for (int v = 0; v < 4; ++v) s_part[w][4 * (lane >> 4) + v][lane & 15] = acc[v];
   __syncthreads();
-  if (t < 256) {
-    const int mm = t >> 4, nc = t & 15;
+  if (t_regs) {
+    // T planes summed in a fixed order
+    const int plane = p.M * p.r;
+    for (int i = t; i < plane; i += nthr) {
+      float sum = 0.0f;
+      for (int z = 0; z < p.tsplits; ++z) sum += s_tp[z * plane + i];
+      s_T[i] = sum;
+      if (p.T_out != nullptr && blockIdx.x == 0) p.T_out[i] = sum;
+    }
+    __syncthreads();
+  }
+  for (int i = t; i < p.M * 16; i += nthr) {
+    const int mm = i >> 4, nc = i & 15;
     const int64_t nn = n0 + nc;
-    if (mm < p.M && nn < p.o) {
+    if (nn < p.o) {
       float y = 0.0f;
-#pragma unroll
-      for (int ww = 0; ww < WAVES; ++ww) y += s_part[ww][mm][nc];
+      for (int ww = 0; ww < nw; ++ww) y += s_part[(ww * 16 + mm) * 17 + nc];
       if (lora) {
         float l = 0.0f;
         for (int j = 0; j < p.r; ++j) l += s_T[mm * p.r + j] * s_B[j * 16 + nc];
@@ -304,6 +476,33 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(GemvArgs p) {
 }
 
 int gemv_tsplits(int64_t d) { return (int)((d + kPrepK - 1) / kPrepK); }
+
+namespace {
+struct GemvPlan {
+  int nw, mx, rr;
+  bool t_regs;
+  int lds;
+};
+GemvPlan gemv_plan(int M, int64_t d, int r, bool lora, bool want_t) {
+  GemvPlan g{};
+  const int64_t nblk = d / kBlock;
+  const int64_t chunks = (nblk + 15) / 16;
+  g.nw = (int)std::min<int64_t>(kGemvMaxWaves, std::max<int64_t>(1, chunks));
+  g.mx = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 16;
+  g.rr = r;
+  const int ts = gemv_tsplits(d);
+  g.t_regs = want_t && (int64_t)ts * M * r <= 4 * g.nw * 64;
+  if (g.t_regs && gemv_smem(g.nw, g.mx, M, r, ts, true).bytes > kGemvMaxLds) g.t_regs = false;
+  g.lds = gemv_smem(g.nw, g.mx, M, r, ts, g.t_regs).bytes;
+  (void)lora;
+  return g;
+}
+}  // namespace
+
+bool gemv_fits(int64_t M, int64_t d, int64_t r) {
+  if (M < 1 || M > kGemvMaxTokens || r > kMaxGemvRank || d % kBlock != 0) return false;
+  return gemv_plan((int)M, d, (int)r, r > 0, r > 0).lds <= kGemvMaxLds;
+}
 
 hipError_t launch_gemv_fwd(const uint16_t* X, int M, int64_t d, const uint8_t* codes,
                            const uint8_t* scale8, const float* scale2, int64_t o,
@@ -317,14 +516,18 @@ hipError_t launch_gemv_fwd(const uint16_t* X, int M, int64_t d, const uint8_t* c
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  GemvArgs p{X, codes, scale8, scale2, Tpart, B, Y, T_out, d, o, M, rr, ts, s, cb};
   const unsigned grid = (unsigned)((o + 15) / 16);
-  // enough waves to keep every CU streaming: split the reduction 4 ways
-  // when there are many row groups, 8 ways otherwise
-  if (o >= 16 * 512)
-    hipLaunchKernelGGL(k_gemv<4>, dim3(grid), dim3(256), 0, st, p);
-  else
-    hipLaunchKernelGGL(k_gemv<8>, dim3(grid), dim3(512), 0, st, p);
+  const bool lora = rr > 0 && s != 0.0f;
+  const GemvPlan g = gemv_plan(M, d, rr, lora, lora || T_out != nullptr);
+  if (g.lds > kGemvMaxLds) return hipErrorInvalidConfiguration;
+  GemvArgs p{X, codes, scale8, scale2, Tpart, B, Y, T_out, d, o, M, rr, ts, g.t_regs ? 1 : 0, s, cb};
+  const size_t lds = (size_t)g.lds;
+  switch (g.mx) {
+    case 1: hipLaunchKernelGGL(k_gemv<1>, dim3(grid), dim3(64 * g.nw), lds, st, p); break;
+    case 2: hipLaunchKernelGGL(k_gemv<2>, dim3(grid), dim3(64 * g.nw), lds, st, p); break;
+    case 4: hipLaunchKernelGGL(k_gemv<4>, dim3(grid), dim3(64 * g.nw), lds, st, p); break;
+    default: hipLaunchKernelGGL(k_gemv<16>, dim3(grid), dim3(64 * g.nw), lds, st, p); break;
+  }
   return hipGetLastError();
 }
 

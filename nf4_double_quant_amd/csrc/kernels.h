@@ -48,6 +48,9 @@ hipError_t launch_fill_zero_bf16(uint16_t* y, int64_t n, hipStream_t st);
 constexpr int kGemvMaxTokens = 16;
 constexpr int kMaxGemvRank = 256;
 int gemv_tsplits(int64_t d);
+// Whether the few-token kernel serves these sizes (its shared memory and
+// staged scales fit); otherwise the forward takes the GEMM path.
+bool gemv_fits(int64_t M, int64_t d, int64_t r);
 hipError_t launch_gemv_fwd(const uint16_t* X, int M, int64_t d, const uint8_t* codes,
                            const uint8_t* scale8, const float* scale2, int64_t o,
                            const uint16_t* A, const uint16_t* B, int r, float s, uint16_t* Y,
