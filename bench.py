@@ -12,7 +12,9 @@ s = 2, W ~ N(0, 0.02), X, dY ~ N(0, 1), A, B ~ N(0, 0.02).
 `value` is algorithmic fwd+bwd TFLOP/s, 4·M·d·o + 6·M·r·(d+o) FLOP per step
 (quantize and dequant count no FLOPs; their time is included).  The JSON line
 also carries the dominant kernel's roofline, the few-token dequant-GEMV
-bandwidth on the 7B-style MLP weights, and the CPU oracle timed on the host.
+bandwidth on the 7B-style MLP weights, the quantization error of each 4-bit
+table (NF4, int4, FP4 E2M1, FP4 E3M0) on the workload's weight, and the CPU
+oracle timed on the host.
 """
 
 from __future__ import annotations
@@ -240,6 +242,7 @@ def main():
                  for name, (ms, n) in per_class.items() if n}
 
     decode = None if args.no_decode else bench_decode(args, qb, torch, np, synth, dev)
+    formats = format_errors(qb, torch, W)
     cpu = None if args.no_cpu_baseline else cpu_baseline(args, wl, p)
 
     out = {
@@ -255,7 +258,8 @@ def main():
                    "step": "quantize NF4+DQ + fwd + bwd (dX, dA, dB)", "flop_per_step": flops,
                    "parallelism": "single GPU"},
         "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
-        "roofline": roofline, "breakdown": breakdown, "decode": decode, "cpu_baseline": cpu,
+        "roofline": roofline, "breakdown": breakdown, "decode": decode, "formats": formats,
+        "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
 
@@ -356,6 +360,19 @@ def bench_decode(args, qb, torch, np, synth, dev):
                         "gemv_kernel_us": round(gemv_ms * 1e3 / max(gemv_n, 1), 2) if gemv_n else None}
     return {"workload": "decode_mlp_7b: gate/up 4096->11008, down 11008->4096, r=16, fwd only",
             "weight_sets_cycled": len(sets), "peak_GBps": PEAK_HBM_GBPS, **res}
+
+
+def format_errors(qb, torch, W):
+    """Quantization error of each 4-bit table on the workload's weight, all
+    on the GPU: blockwise 4-bit + double quantization, dequant to fp32, mean
+    squared error against W (and over W's variance)."""
+    var = float(W.double().var())
+    out = {}
+    for fmt in qb.FORMATS:
+        q = qb.qlora_quantize_nf4_dq(W, check_finite=False, fmt=fmt)
+        mse = float(((qb.qlora_dequant(q).double() - W.double()) ** 2).mean())
+        out[fmt] = {"mse": mse, "mse_over_var": round(mse / var, 5)}
+    return out
 
 
 def cpu_baseline(args, wl, p):
