@@ -18,7 +18,10 @@ Sources (cited by page title and section):
   self-constructed 16384-weight example), the note on what the backward pass
   still needs, and §三 (the training procedure and the 4096×4096 example).
 * [QLoRA-glossary] weimeta.cn glossary entry "QLoRA", section "NF4 4-bit
-  量化是什么" (NF4 cuts the normal curve into 16 quantile intervals).
+  量化是什么" (NF4 cuts the normal curve into 16 quantile intervals), and
+  its FAQ on deployment (one 4-bit base, unmerged adapters per customer).
+* [LoRA-PyTorch] "深入理解 LoRA 与 QLoRA低秩自适应微调的矩阵分解原理与
+  PyTorch 高效实现" (mhpn.cn), §四.5 on switching between several adapters.
 
 Arithmetic is fp64 (or exact) except where the method fixes fp32 / bf16
 storage: the codebook and the scales are fp32 values, the dequantized weight
@@ -27,6 +30,8 @@ is an fp32 product rounded to bf16.
 Modules:
   nf4     -- codebook, blockwise NF4 encode, double quantization, dequant.
   linear  -- forward / backward of Y = X·Ŵ + s·X·A·B in fp64.
+  formats -- the int4 / FP4 comparison tables through the same scheme.
+  multi   -- one base with a LoRA adapter chosen per token.
 """
 
-from . import nf4, linear  # noqa: F401
+from . import nf4, linear, formats, multi  # noqa: F401
