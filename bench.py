@@ -264,6 +264,60 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+def _time_decode(qb, torch, sets, one, ys, byts, K_GEMV):
+    """Time one MLP pass over every weight set: eager, then as a HIP-graph replay."""
+    for layer in sets:
+        one(layer)
+    torch.cuda.synchronize()
+    reps = max(2, 96 // len(sets))
+    # per-launch kernel time of the dequant-GEMV (eager, HIP events on the stream)
+    qb.qlora_timing_begin([K_GEMV])
+    for layer in sets:
+        one(layer)
+    torch.cuda.synchronize()
+    qb.qlora_timing_end()
+    gemv_ms, gemv_n = qb.qlora_timing_read(K_GEMV)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # eager: one Python call per projection (host launch cost included)
+    e0.record()
+    for _ in range(reps):
+        for layer in sets:
+            one(layer)
+    e1.record()
+    torch.cuda.synchronize()
+    us_eager = e0.elapsed_time(e1) * 1e3 / (reps * len(sets))
+    # the same launches captured once in a HIP graph and replayed: the GPU time
+    us, graph_ok = None, None
+    try:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for layer in sets:
+                one(layer)
+        for _ in range(2):
+            g.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (reps * len(sets))
+        # every replay leaves the last set's outputs: compare with eager calls
+        got = {k: v.clone() for k, v in ys.items()}
+        one(sets[-1])
+        torch.cuda.synchronize()
+        graph_ok = all(torch.equal(got[k], ys[k]) for k in ys)
+    except Exception as e:  # capture unsupported: report the eager figure only
+        print(f"decode graph capture failed: {e}", file=sys.stderr)
+    t = us if (us is not None and graph_ok) else us_eager
+    return {"us_per_mlp": round(t, 2), "timing": "hip_graph" if t is us else "eager",
+            "us_per_mlp_eager": round(us_eager, 2), "graph_replay_matches_eager": graph_ok,
+            "bytes_per_mlp": byts,
+            "GBps": round(byts / (t * 1e-6) / 1e9, 1),
+            "frac_of_hbm": round(byts / (t * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+            "gemv_kernel_us": round(gemv_ms * 1e3 / max(gemv_n, 1), 2) if gemv_n else None}
+
+
 def bench_decode(args, qb, torch, np, synth, dev):
     """Few-token forward on 7B-style gate/up/down NF4 weights, rank 16, cycling
     independent weight sets so the 256 MB MALL cannot hold them."""
@@ -308,57 +362,32 @@ def bench_decode(args, qb, torch, np, synth, dev):
                 A, B = adapters[p.name]
                 qb.qlora_linear_fwd(xs[p.name], qw, A, B, wl.s, want_T=False, ws=ws, out=ys[p.name])
 
-        for layer in sets:
-            one(layer)
-        torch.cuda.synchronize()
-        reps = max(2, 96 // len(sets))
-        # per-launch kernel time of the dequant-GEMV (eager, HIP events on the stream)
-        qb.qlora_timing_begin([qb.K_GEMV])
-        for layer in sets:
-            one(layer)
-        torch.cuda.synchronize()
-        qb.qlora_timing_end()
-        gemv_ms, gemv_n = qb.qlora_timing_read(qb.K_GEMV)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        # eager: one Python call per projection (host launch cost included)
-        e0.record()
-        for _ in range(reps):
-            for layer in sets:
-                one(layer)
-        e1.record()
-        torch.cuda.synchronize()
-        us_eager = e0.elapsed_time(e1) * 1e3 / (reps * len(sets))
-        # the same launches captured once in a HIP graph and replayed: the GPU time
-        us, graph_ok = None, None
-        try:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                for layer in sets:
-                    one(layer)
-            for _ in range(2):
-                g.replay()
-            torch.cuda.synchronize()
-            e0.record()
-            for _ in range(reps):
-                g.replay()
-            e1.record()
-            torch.cuda.synchronize()
-            us = e0.elapsed_time(e1) * 1e3 / (reps * len(sets))
-            # every replay leaves the last set's outputs: compare with eager calls
-            got = {k: v.clone() for k, v in ys.items()}
-            one(sets[-1])
-            torch.cuda.synchronize()
-            graph_ok = all(torch.equal(got[k], ys[k]) for k in ys)
-        except Exception as e:  # capture unsupported: report the eager figure only
-            print(f"decode graph capture failed: {e}", file=sys.stderr)
-        t = us if (us is not None and graph_ok) else us_eager
-        res[f"M{M}"] = {"us_per_mlp": round(t, 2), "timing": "hip_graph" if t is us else "eager",
-                        "us_per_mlp_eager": round(us_eager, 2), "graph_replay_matches_eager": graph_ok,
-                        "bytes_per_mlp": byts,
-                        "GBps": round(byts / (t * 1e-6) / 1e9, 1),
-                        "frac_of_hbm": round(byts / (t * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
-                        "gemv_kernel_us": round(gemv_ms * 1e3 / max(gemv_n, 1), 2) if gemv_n else None}
-    return {"workload": "decode_mlp_7b: gate/up 4096->11008, down 11008->4096, r=16, fwd only",
+        res[f"M{M}"] = _time_decode(qb, torch, sets, one, ys, byts, K_GEMV=qb.K_GEMV)
+
+    # one adapter per token: 16 tokens on 16 different rank-16 adapters per projection
+    M, n_ad = 16, 16
+    multi_ad = {p.name: (bfd(synth.normal_bf16((n_ad, p.d, wl.r), 0.02, [wl.wid, synth.PROJ_IDS[p.name], synth.T_A_STACK])),
+                         bfd(synth.normal_bf16((n_ad, wl.r, p.o), 0.02, [wl.wid, synth.PROJ_IDS[p.name], synth.T_B_STACK])))
+                for p in wl.projs}
+    s_list = [wl.s] * n_ad
+    idx = torch.arange(M, dtype=torch.int32, device=dev)
+    xs = {p.name: torch.from_numpy(synth.normal_bf16((M, p.d), 1.0, [wl.wid, synth.PROJ_IDS[p.name],
+                                                                     synth.T_X]).view(np.int16))
+          .view(torch.bfloat16).to(dev) for p in wl.projs}
+    ys = {p.name: torch.empty((M, p.o), dtype=torch.bfloat16, device=dev) for p in wl.projs}
+    byts = 0
+    for p in wl.projs:
+        c, s8, s2 = qb.qlora_quant_sizes(p.o * p.d)
+        byts += c + s8 + s2 + 2 * (n_ad * (p.d * wl.r + wl.r * p.o) + M * p.d + M * p.o)
+
+    def one_multi(layer):
+        for p, qw in layer:
+            A, B = multi_ad[p.name]
+            qb.qlora_linear_fwd_multi(xs[p.name], qw, A, B, s_list, idx, ws=ws, out=ys[p.name])
+
+    res["M16_16_adapters"] = _time_decode(qb, torch, sets, one_multi, ys, byts, K_GEMV=qb.K_GEMV)
+    return {"workload": "decode_mlp_7b: gate/up 4096->11008, down 11008->4096, r=16, fwd only; "
+                        "M16_16_adapters: one adapter per token (16 adapters per projection)",
             "weight_sets_cycled": len(sets), "peak_GBps": PEAK_HBM_GBPS, **res}
 
 

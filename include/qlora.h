@@ -63,6 +63,8 @@ extern "C" {
 #define QLORA_MAX_RANK 256  /* largest LoRA rank r accepted                  */
 #define QLORA_MAX_DIM (1LL << 20)       /* largest d and o of a linear layer  */
 #define QLORA_MAX_WEIGHTS (1LL << 31)   /* largest o*d of a linear layer      */
+#define QLORA_MAX_MULTI_TOKENS 16       /* largest M of qlora_linear_fwd_multi */
+#define QLORA_MAX_ADAPTERS 64           /* largest adapter count of the same   */
 
 typedef enum {
   QLORA_OK = 0,
@@ -159,8 +161,8 @@ const char* qlora_version(void);
 int qlora_quantize_nf4_dq(const float* W, int64_t n, const qlora_nf4dq* out,
                           int32_t* d_flags, void* stream);
 
-/* Dequantization Ŵ = Dequant(W4bit, scales) (QLoRA-074 §一; §三 "dequantize
- * the required weights to BF16").
+/* Dequantization Ŵ = Dequant(W4bit, scales) (QLoRA-074 §一; §三: the
+ * weights a product needs are dequantized to BF16 on demand).
  *   q          quantized tensor (device buffers), q->n >= 0.
  *   out_dtype  QLORA_F32: out is fp32[n] with ŵ_i = fl32(V[k]·fl32(q8·step));
  *              QLORA_BF16: out is bf16[n] holding RNE_bf16(ŵ_i).
@@ -183,6 +185,29 @@ int qlora_linear_fwd(const qlora_bf16* X, int64_t M, int64_t d,
                      const qlora_bf16* A, const qlora_bf16* B, int64_t r, float s,
                      qlora_bf16* Y, float* T_out,
                      void* ws, size_t ws_bytes, void* stream);
+
+/* Few-token forward with one LoRA adapter per token over one shared frozen
+ * base: several independent adapter pairs sit beside the 4-bit base and each
+ * request picks one (LoRA-PyTorch page §四.5; the weimeta QLoRA glossary's
+ * FAQ on serving customers from one unmerged 4-bit base).  For each row m:
+ *     a = d_adapter[m],   T[m] = X[m]·A[a],   Y[m] = X[m]·Ŵ + s[a]·T[m]·B[a]
+ * and an index outside [0, n_adapters) selects the base alone (T[m] = 0).
+ *   X          bf16[M][d], 1 <= M <= QLORA_MAX_MULTI_TOKENS (M == 0: no-op)
+ *   W          quantized Wq[o][d] as for qlora_linear_fwd
+ *   A          bf16[n_adapters][d][r], B bf16[n_adapters][r][o] (device)
+ *   s          host float[n_adapters]; 1 <= n_adapters <= QLORA_MAX_ADAPTERS
+ *   d_adapter  device int32[M]
+ *   Y          bf16[M][o] (overwritten); T_out fp32[M][r] or NULL
+ *   ws         workspace of qlora_workspace_bytes(QLORA_OP_FWD, M, d, o, r)
+ * 8 <= r <= 256, r % 8 == 0.  A row whose adapter is a gives bitwise the
+ * result of qlora_linear_fwd with (A[a], B[a], s[a]).  QLORA_E_SHAPE also
+ * when the few-token kernel cannot serve these sizes (d above 65536 with a
+ * large M·r). */
+int qlora_linear_fwd_multi(const qlora_bf16* X, int64_t M, int64_t d,
+                           const qlora_nf4dq* W, int64_t o, const qlora_bf16* A,
+                           const qlora_bf16* B, int64_t n_adapters, int64_t r,
+                           const float* s, const int32_t* d_adapter, qlora_bf16* Y,
+                           float* T_out, void* ws, size_t ws_bytes, void* stream);
 
 /* Backward of the QLoRA linear layer (QLoRA-074 §一 and the note on what the
  * backward pass still needs): with U = dY·Bᵀ,

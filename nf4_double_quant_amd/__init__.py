@@ -7,7 +7,8 @@ built, or a tensor is not on a HIP device, the calls raise.
 
 Functions carry the C names:
   qlora_quant_sizes, qlora_codebook, qlora_workspace_bytes,
-  qlora_quantize_nf4_dq, qlora_dequant, qlora_linear_fwd, qlora_linear_bwd.
+  qlora_quantize_nf4_dq, qlora_dequant, qlora_linear_fwd, qlora_linear_bwd,
+  qlora_linear_fwd_multi.
 """
 
 from __future__ import annotations
@@ -63,10 +64,13 @@ def lib() -> ctypes.CDLL:
                                    vp, vp, vp, sz, vp]
     L.qlora_linear_bwd.argtypes = [vp, vp, vp, i64, i64, P(_NF4DQ), i64, vp, vp, i64,
                                    ctypes.c_float, vp, vp, vp, vp, sz, vp]
+    L.qlora_linear_fwd_multi.argtypes = [vp, i64, i64, P(_NF4DQ), i64, vp, vp, i64, i64,
+                                         P(ctypes.c_float), vp, vp, vp, vp, sz, vp]
     L.qlora_timing_begin.argtypes = [ctypes.c_uint32]
     L.qlora_timing_read.argtypes = [i32, P(ctypes.c_double), P(i64)]
     for name in ("qlora_quant_sizes", "qlora_codebook", "qlora_quantize_nf4_dq", "qlora_dequant",
-                 "qlora_linear_fwd", "qlora_linear_bwd", "qlora_timing_begin", "qlora_timing_end",
+                 "qlora_linear_fwd", "qlora_linear_bwd", "qlora_linear_fwd_multi",
+                 "qlora_timing_begin", "qlora_timing_end",
                  "qlora_timing_read"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
@@ -295,3 +299,35 @@ def qlora_linear_bwd(dY, X, T, q: QuantizedWeight, A, B, s: float, need_dX: bool
                                   _ptr(A), _ptr(B), r, float(s), _ptr(dX), _ptr(dA), _ptr(dB),
                                   _ptr(buf), buf.numel(), _stream(dev)), "qlora_linear_bwd")
     return dX, dA, dB
+
+
+def qlora_linear_fwd_multi(X, q: QuantizedWeight, A, B, s, adapter, want_T: bool = False,
+                           ws=None, out=None):
+    """Few-token forward with one adapter per token over one shared base.
+
+    X bf16 [M][d] (M <= 16); A bf16 [n][d][r]; B bf16 [n][r][o]; s: n floats;
+    adapter: int32 device tensor [M], an index outside [0, n) selecting the
+    base alone.  Returns (Y, T) with T = X[m]·A[adapter[m]] in fp32 (or None).
+    """
+    torch = _torch()
+    M, d = X.shape
+    o = q.shape[0]
+    n, _, r = A.shape
+    for t, nm in ((X, "X"), (A, "A"), (B, "B")):
+        _need(t, torch.bfloat16, nm, X.device)
+    _need(adapter, torch.int32, "adapter", X.device)
+    if adapter.numel() != M:
+        raise ValueError("adapter must hold one index per token")
+    svals = [float(v) for v in s]
+    if len(svals) != n:
+        raise ValueError("s must hold one scale per adapter")
+    Y = torch.empty((M, o), dtype=torch.bfloat16, device=X.device) if out is None else out
+    _need(Y, torch.bfloat16, "Y", X.device)
+    T = torch.empty((M, r), dtype=torch.float32, device=X.device) if want_T else None
+    nbytes = qlora_workspace_bytes(QLORA_OP_FWD, M, d, o, r)
+    buf = _workspace(ws, X.device, nbytes)
+    s_arr = (ctypes.c_float * n)(*svals)
+    _check(lib().qlora_linear_fwd_multi(_ptr(X), M, d, ctypes.byref(q.view()), o, _ptr(A), _ptr(B),
+                                        n, r, s_arr, _ptr(adapter), _ptr(Y), _ptr(T), _ptr(buf),
+                                        buf.numel(), _stream(X.device)), "qlora_linear_fwd_multi")
+    return Y, T

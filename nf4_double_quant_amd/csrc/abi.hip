@@ -270,6 +270,33 @@ int qlora_linear_fwd(const qlora_bf16* X, int64_t M, int64_t d, const qlora_nf4d
   return QLORA_OK;
 }
 
+int qlora_linear_fwd_multi(const qlora_bf16* X, int64_t M, int64_t d, const qlora_nf4dq* W,
+                           int64_t o, const qlora_bf16* A, const qlora_bf16* B, int64_t n_adapters,
+                           int64_t r, const float* s, const int32_t* d_adapter, qlora_bf16* Y,
+                           float* T_out, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_linear_shapes(M, d, o, r, W);
+  if (st) return st;
+  if (M > QLORA_MAX_MULTI_TOKENS || r < 8) return QLORA_E_SHAPE;
+  if (n_adapters < 1 || n_adapters > QLORA_MAX_ADAPTERS) return QLORA_E_SHAPE;
+  if (M > 0 && (X == nullptr || Y == nullptr || d_adapter == nullptr)) return QLORA_E_INVALID;
+  if (A == nullptr || B == nullptr || s == nullptr) return QLORA_E_INVALID;
+  if (!aligned16(X) || !aligned16(Y) || !aligned16(A) || !aligned16(B) || !aligned16(T_out) ||
+      !aligned16(ws) || (reinterpret_cast<uintptr_t>(d_adapter) & 3) != 0)
+    return QLORA_E_ALIGN;
+  const FwdLayout L = fwd_layout(M, d, o, r);
+  if (M > 0 && !L.gemv) return QLORA_E_SHAPE;
+  if (ws_bytes < (size_t)L.total) return QLORA_E_WORKSPACE;
+  if (L.total > 0 && ws == nullptr) return QLORA_E_WORKSPACE;
+  if (M == 0) return QLORA_OK;
+  if ((st = device_status())) return st;
+  hipStream_t hs = (hipStream_t)stream;
+  float* Tpart = reinterpret_cast<float*>(static_cast<char*>(ws) + L.Tpart);
+  QL_RUN(QLORA_K_GEMV, hs,
+         launch_gemv_fwd(X, (int)M, d, W->codes, W->scale8, W->scale2, o, A, B, (int)r, 0.0f, Y,
+                         T_out, Tpart, host_codebook(W->fmt), hs, d_adapter, (int)n_adapters, s));
+  return QLORA_OK;
+}
+
 int qlora_linear_bwd(const qlora_bf16* dY, const qlora_bf16* X, const float* T, int64_t M, int64_t d,
                      const qlora_nf4dq* W, int64_t o, const qlora_bf16* A, const qlora_bf16* B,
                      int64_t r, float s, qlora_bf16* dX, qlora_bf16* dA, qlora_bf16* dB, void* ws,

@@ -38,18 +38,32 @@ __device__ __forceinline__ s16x4 lds_read_tr(const uint16_t* p) {
 }
 
 // Split-K planes of T = X·A for M <= 16: workgroup (z, c) sums k in
-// [512 z, 512 z + 512) for the adapter columns [64 c, 64 c + 64).
+// [512 z, 512 z + 512) for the adapter columns [64 c, 64 c + 64).  With one
+// adapter per token (adapter != null) workgroup layer blockIdx.z serves the
+// single row blockIdx.z with that row's adapter.
 constexpr int kPrepK = 512;
 constexpr int kPrepStride = 80;  // bf16 per LDS row: 64 + 16 pad, conflict-free transposed reads
 
 __global__ __launch_bounds__(256) void k_lora_down_small(const uint16_t* __restrict__ X, int M,
                                                          int64_t d, const uint16_t* __restrict__ A,
-                                                         int r, float* __restrict__ Tpart) {
+                                                         int r, float* __restrict__ Tpart,
+                                                         const int32_t* __restrict__ adapter,
+                                                         int n_ad) {
   __shared__ __attribute__((aligned(16))) uint16_t s_a[kPrepK * kPrepStride];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int64_t k0 = (int64_t)blockIdx.x * kPrepK;
   const int c0 = blockIdx.y * 64;
   const int m = lane & 15, g = lane >> 4, s = lane & 15;
+  int only = -1;                                   // the one row served, or -1 for all
+  if (adapter != nullptr) {
+    only = (int)blockIdx.z;
+    const int a = adapter[only];
+    if (a < 0 || a >= n_ad) {                      // no adapter: T[only] = 0 (whole workgroup)
+      if (t < 64 && c0 + t < r) Tpart[((int64_t)blockIdx.x * M + only) * r + c0 + t] = 0.0f;
+      return;
+    }
+    A += (int64_t)a * d * r;
+  }
   // this lane's activations for its four 32-wide k steps, requested before
   // the adapter tile so that both arrive in one round trip
   uint4 xv[4];
@@ -57,7 +71,8 @@ __global__ __launch_bounds__(256) void k_lora_down_small(const uint16_t* __restr
   for (int q = 0; q < 4; ++q) {
     const int64_t kx = k0 + (w * 4 + q) * 32 + 8 * g;
     xv[q] = make_uint4(0, 0, 0, 0);
-    if (m < M && kx < d) xv[q] = *reinterpret_cast<const uint4*>(X + (int64_t)m * d + kx);
+    if (m < M && kx < d && (only < 0 || m == only))
+      xv[q] = *reinterpret_cast<const uint4*>(X + (int64_t)m * d + kx);
   }
   // stage A[k0:k0+512][c0:c0+64] (zeros outside); all 16 loads of a thread
   // are in flight before the first store
@@ -104,7 +119,7 @@ __global__ __launch_bounds__(256) void k_lora_down_small(const uint16_t* __restr
   __syncthreads();
   for (int i = t; i < 16 * 64; i += 256) {
     const int mm = i >> 6, cc = i & 63;
-    if (mm < M && c0 + cc < r) {
+    if (mm < M && c0 + cc < r && (only < 0 || mm == only)) {
       const float v = red[(0 * 16 + mm) * 64 + cc] + red[(1 * 16 + mm) * 64 + cc] +
                       red[(2 * 16 + mm) * 64 + cc] + red[(3 * 16 + mm) * 64 + cc];
       Tpart[((int64_t)blockIdx.x * M + mm) * r + c0 + cc] = v;
@@ -127,6 +142,9 @@ struct GemvArgs {
   int t_regs;           // 1: T planes fit the register path (host-checked LDS size)
   float s;
   Codebook cb;
+  const int32_t* adapter;  // one adapter per token ([M]), or null
+  int n_ad;
+  float s_ad[kMaxAdapters];
 };
 
 // Byte planes of a 16-entry bf16 table given as 8 dwords (entries 2i, 2i+1).
@@ -232,11 +250,12 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void k_gemv(GemvArgs p) {
   const uint32_t ngrp = (nblk + 3) / 4;
   const int nl = lane & 15, q = lane >> 4, m = lane & 15;
   const int64_t n = n0 + nl;
-  const bool lora = p.r > 0 && p.s != 0.0f;
+  const bool multi = p.adapter != nullptr;
+  const bool lora = p.r > 0 && (multi || p.s != 0.0f);
   const bool want_t = lora || (p.T_out != nullptr && blockIdx.x == 0);
   const int tpl = p.tsplits * p.M * p.r;                    // T-plane elements
   const bool t_regs = want_t && p.t_regs != 0;
-  const bool b_regs = lora && p.r * 8 <= 2 * nthr;
+  const bool b_regs = lora && !multi && p.r * 8 <= 2 * nthr;
   const GemvSmem L = gemv_smem(nw, MX, p.M, p.r, p.tsplits, p.t_regs != 0);
   float* s_part = reinterpret_cast<float*>(smem + L.part);  // [nw][16][17]
   float* s_tp = reinterpret_cast<float*>(smem + L.tp);      // [tsplits][M][r]
@@ -424,7 +443,7 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void k_gemv(GemvArgs p) {
         s_B[2 * i + 1] = bf16_to_f32((uint16_t)(bb[u] >> 16));
       }
     }
-  } else if (lora) {
+  } else if (lora && !multi) {
     for (int i = t; i < p.r * 16; i += nthr) {
       const int j = i >> 4, c = i & 15;
       s_B[i] = n0 + c < p.o ? bf16_to_f32(p.B[(int64_t)j * p.o + n0 + c]) : 0.0f;
@@ -465,10 +484,19 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void k_gemv(GemvArgs p) {
     if (nn < p.o) {
       float y = 0.0f;
       for (int ww = 0; ww < nw; ++ww) y += s_part[(ww * 16 + mm) * 17 + nc];
-      if (lora) {
+      if (lora && !multi) {
         float l = 0.0f;
         for (int j = 0; j < p.r; ++j) l += s_T[mm * p.r + j] * s_B[j * 16 + nc];
         y += p.s * l;
+      } else if (lora) {
+        // this row's adapter (same products, same order as the single case)
+        const int a = p.adapter[mm];
+        if (a >= 0 && a < p.n_ad) {
+          const uint16_t* Ba = p.B + ((int64_t)a * p.r) * p.o + nn;
+          float l = 0.0f;
+          for (int j = 0; j < p.r; ++j) l += s_T[mm * p.r + j] * bf16_to_f32(Ba[(int64_t)j * p.o]);
+          y += p.s_ad[a] * l;
+        }
       }
       p.Y[(int64_t)mm * p.o + nn] = bf16_bits(y);
     }
@@ -507,20 +535,25 @@ bool gemv_fits(int64_t M, int64_t d, int64_t r) {
 hipError_t launch_gemv_fwd(const uint16_t* X, int M, int64_t d, const uint8_t* codes,
                            const uint8_t* scale8, const float* scale2, int64_t o,
                            const uint16_t* A, const uint16_t* B, int r, float s, uint16_t* Y,
-                           float* T_out, float* Tpart, const Codebook& cb, hipStream_t st) {
+                           float* T_out, float* Tpart, const Codebook& cb, hipStream_t st,
+                           const int32_t* adapter, int n_ad, const float* s_ad) {
   const int ts = gemv_tsplits(d);
-  const int rr = (r > 0 && (s != 0.0f || T_out != nullptr)) ? r : 0;
+  const bool multi = adapter != nullptr;
+  if (multi && (n_ad < 1 || n_ad > kMaxAdapters || s_ad == nullptr)) return hipErrorInvalidValue;
+  const int rr = (r > 0 && (multi || s != 0.0f || T_out != nullptr)) ? r : 0;
   if (rr > 0) {
-    hipLaunchKernelGGL(k_lora_down_small, dim3(ts, (rr + 63) / 64), dim3(256), 0, st, X, M, d, A,
-                       rr, Tpart);
+    hipLaunchKernelGGL(k_lora_down_small, dim3(ts, (rr + 63) / 64, multi ? M : 1), dim3(256), 0, st,
+                       X, M, d, A, rr, Tpart, adapter, n_ad);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const unsigned grid = (unsigned)((o + 15) / 16);
-  const bool lora = rr > 0 && s != 0.0f;
+  const bool lora = rr > 0 && (multi || s != 0.0f);
   const GemvPlan g = gemv_plan(M, d, rr, lora, lora || T_out != nullptr);
   if (g.lds > kGemvMaxLds) return hipErrorInvalidConfiguration;
-  GemvArgs p{X, codes, scale8, scale2, Tpart, B, Y, T_out, d, o, M, rr, ts, g.t_regs ? 1 : 0, s, cb};
+  GemvArgs p{X, codes, scale8, scale2, Tpart, B, Y, T_out, d, o, M, rr, ts, g.t_regs ? 1 : 0, s, cb,
+             adapter, multi ? n_ad : 0, {}};
+  for (int i = 0; multi && i < n_ad; ++i) p.s_ad[i] = s_ad[i];
   const size_t lds = (size_t)g.lds;
   switch (g.mx) {
     case 1: hipLaunchKernelGGL(k_gemv<1>, dim3(grid), dim3(64 * g.nw), lds, st, p); break;

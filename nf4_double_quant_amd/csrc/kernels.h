@@ -51,9 +51,14 @@ int gemv_tsplits(int64_t d);
 // Whether the few-token kernel serves these sizes (its shared memory and
 // staged scales fit); otherwise the forward takes the GEMM path.
 bool gemv_fits(int64_t M, int64_t d, int64_t r);
+// adapter != null: one adapter per token, A [n_ad][d][r], B [n_ad][r][o],
+// scales s_ad[n_ad] (host); an index outside [0, n_ad) selects no adapter.
+constexpr int kMaxAdapters = 64;
 hipError_t launch_gemv_fwd(const uint16_t* X, int M, int64_t d, const uint8_t* codes,
                            const uint8_t* scale8, const float* scale2, int64_t o,
                            const uint16_t* A, const uint16_t* B, int r, float s, uint16_t* Y,
-                           float* T_out, float* Tpart, const Codebook& cb, hipStream_t st);
+                           float* T_out, float* Tpart, const Codebook& cb, hipStream_t st,
+                           const int32_t* adapter = nullptr, int n_ad = 0,
+                           const float* s_ad = nullptr);
 
 }  // namespace qlora

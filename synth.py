@@ -18,6 +18,7 @@ from dataclasses import dataclass
 import numpy as np
 
 T_W, T_X, T_A, T_B, T_DY = 0, 1, 2, 3, 4
+T_A_STACK, T_B_STACK = 7, 8        # stacked adapters [n][d][r], [n][r][o] (one per token)
 
 
 def normal_f32(shape, std: float, seed) -> np.ndarray:

@@ -140,6 +140,23 @@ def test_validation_statuses(L):
                A16, 1 << 30, None) == 1                     # dA missing
 
 
+def test_multi_adapter_validation(L):
+    f = L.qlora_linear_fwd_multi
+    v = _view(128 * 128)
+    s = (ctypes.c_float * 64)(*([1.0] * 64))
+
+    def call(M=4, n=3, r=16, adapter=A16, A=A16, sp=s, view=v):
+        return f(A16, M, 128, ctypes.byref(view), 128, A, A16, n, r, sp, adapter, A16, None, A16,
+                 1 << 30, None)
+
+    assert call(M=17) == 2                   # above QLORA_MAX_MULTI_TOKENS
+    assert call(n=0) == 2 and call(n=65) == 2
+    assert call(r=0) == 2 and call(r=12) == 2
+    assert call(adapter=None) == 1 and call(A=None) == 1 and call(sp=None) == 1
+    assert call(adapter=A16 + 2) == 3        # int32 indices must be 4-byte aligned
+    assert call(view=_view(128 * 128, fmt=9)) == 1
+
+
 def test_no_device_status(L):
     import torch
     if torch.cuda.is_available():
