@@ -32,6 +32,7 @@ Modules:
   linear  -- forward / backward of Y = X·Ŵ + s·X·A·B in fp64.
   formats -- the int4 / FP4 comparison tables through the same scheme.
   multi   -- one base with a LoRA adapter chosen per token.
+  merge   -- the adapter merged into the base, then quantized again.
 """
 
-from . import nf4, linear, formats, multi  # noqa: F401
+from . import nf4, linear, formats, multi, merge  # noqa: F401
