@@ -16,7 +16,9 @@ Sources (cited by page title and section):
   "frozen" means), §二 NF4 / double quantization, the boxed note on counting
   quantization constants in the compression ratio (including the
   self-constructed 16384-weight example), the note on what the backward pass
-  still needs, and §三 (the training procedure and the 4096×4096 example).
+  still needs, §三 (the training procedure and the 4096×4096 example), §四
+  Table 2 (the 4-bit format comparison) and §五/§六 on merging an adapter and
+  quantizing again.
 * [QLoRA-glossary] weimeta.cn glossary entry "QLoRA", section "NF4 4-bit
   量化是什么" (NF4 cuts the normal curve into 16 quantile intervals), and
   its FAQ on deployment (one 4-bit base, unmerged adapters per customer).

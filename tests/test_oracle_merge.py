@@ -1,9 +1,10 @@
 """Pins of the merge-and-requantize oracle.
 
-The merged weight is pinned against exact rational arithmetic on small
-inputs, against a plain fp64 matrix product (to within one fp32 ulp, with
-almost every element identical), and against the cases where the merge must
-leave the base untouched (s = 0, zero adapter).
+The merged weight is pinned against the exact value (rational arithmetic on
+small inputs, an fp64 matrix product at larger ones) within the error bound
+of r sequential fp32 roundings plus two more, against the fp32 rounding of
+the exact result for most elements, and against the cases where the
+merge must leave the base untouched (s = 0, zero adapter).
 """
 
 from fractions import Fraction
@@ -29,26 +30,46 @@ def _case(o=24, d=64, r=8, seed=3):
     return w_hat, A, B
 
 
+U = 2.0 ** -24          # unit roundoff of fp32
+
+
+def _bound(w_hat, A, B, s, r):
+    """|fl(merge) - exact| <= |s|·(r+1)·u·Σ_j|A B| + u·|ŵ + sΔ| (+ u² terms)."""
+    absum = np.abs(A) @ np.abs(B)                     # [d][o]
+    exact = w_hat.astype(np.float64) + s * (A @ B).T
+    return abs(s) * (r + 1) * U * absum.T * 1.0001 + U * np.abs(exact) * 1.0001, exact
+
+
 def test_exact_rational_on_small_inputs():
     w_hat, A, B = _case(o=8, d=64, r=8)
     s = 2.0
     got = merge.merge(w_hat, A, B, s)
+    bound, _ = _bound(w_hat, A, B, s, 8)
     for n in range(8):
         for k in range(0, 64, 7):
             exact = Fraction(float(w_hat[n, k])) + Fraction(s) * sum(
                 Fraction(float(A[k, j])) * Fraction(float(B[j, n])) for j in range(8))
-            want = np.float32(float(exact))          # nearest fp32 of the exact value
-            assert got[n, k] == want, (n, k)
+            assert abs(Fraction(float(got[n, k])) - exact) <= Fraction(float(bound[n, k])), (n, k)
 
 
-def test_close_to_a_plain_matrix_product():
-    w_hat, A, B = _case(o=40, d=128, r=16, seed=4)
+def test_within_the_rounding_bound_of_the_exact_merge():
+    w_hat, A, B = _case(o=40, d=128, r=64, seed=4)
     s = 0.5
     got = merge.merge(w_hat, A, B, s)
-    ref = (w_hat.astype(np.float64) + s * (A @ B).T).astype(np.float32)
-    ulp = np.spacing(np.abs(ref))
-    assert np.all(np.abs(got.astype(np.float64) - ref) <= ulp)
-    assert np.mean(got == ref) > 0.999
+    bound, exact = _bound(w_hat, A, B, s, 64)
+    assert np.all(np.abs(got.astype(np.float64) - exact) <= bound)
+    # and mostly the fp32 rounding of the exact value itself (64 fp32
+    # roundings of the rank sum move the last bit of about one in ten)
+    assert np.mean(got == exact.astype(np.float32)) > 0.8
+
+
+def test_a_transposed_or_missing_term_breaks_the_bound():
+    w_hat, A, B = _case(o=32, d=64, r=16, seed=6)
+    bound, exact = _bound(w_hat, A, B, 2.0, 16)
+    wrong = merge.merge(w_hat, A[:, :15], B[:15], 2.0)        # a dropped rank term
+    assert np.any(np.abs(wrong.astype(np.float64) - exact) > bound)
+    wrong = merge.merge(w_hat, A, B, -2.0)                     # a wrong sign
+    assert np.any(np.abs(wrong.astype(np.float64) - exact) > bound)
 
 
 def test_nothing_to_merge_leaves_the_base():
