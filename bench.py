@@ -243,6 +243,7 @@ def main():
 
     decode = None if args.no_decode else bench_decode(args, qb, torch, np, synth, dev)
     formats = format_errors(qb, torch, W)
+    merge_res = merge_study(qb, torch, W, q, X, A, B, s)
     cpu = None if args.no_cpu_baseline else cpu_baseline(args, wl, p)
 
     out = {
@@ -259,6 +260,7 @@ def main():
                    "parallelism": "single GPU"},
         "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "roofline": roofline, "breakdown": breakdown, "decode": decode, "formats": formats,
+        "merge": merge_res,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
@@ -389,6 +391,51 @@ def bench_decode(args, qb, torch, np, synth, dev):
     return {"workload": "decode_mlp_7b: gate/up 4096->11008, down 11008->4096, r=16, fwd only; "
                         "M16_16_adapters: one adapter per token (16 adapters per projection)",
             "weight_sets_cycled": len(sets), "peak_GBps": PEAK_HBM_GBPS, **res}
+
+
+def merge_study(qb, torch, W, q, X, A, B, s):
+    """Merge the adapter into the base, quantize again, and measure how far the
+    merged 4-bit layer's output moves from the unmerged layer's output."""
+    o, d = q.shape
+    r = A.shape[1]
+    for _ in range(3):
+        Wm = qb.qlora_merge_adapter(q, A, B, s)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 20
+    e0.record()
+    for _ in range(reps):
+        qb.qlora_merge_adapter(q, A, B, s, out=Wm)
+    e1.record()
+    torch.cuda.synchronize()
+    us_merge = e0.elapsed_time(e1) * 1e3 / reps
+    q2 = qb.qlora_quantize_nf4_dq(Wm, check_finite=False)
+    e0.record()
+    for _ in range(reps):
+        qb.qlora_quantize_nf4_dq(Wm, check_finite=False, out=q2)
+    e1.record()
+    torch.cuda.synchronize()
+    us_requant = e0.elapsed_time(e1) * 1e3 / reps
+    Y_unmerged, _ = qb.qlora_linear_fwd(X, q, A, B, s, want_T=False)
+    Y_merged, _ = qb.qlora_linear_fwd(X, q2, None, None, 0.0, want_T=False)
+    Y_base, _ = qb.qlora_linear_fwd(X, q, None, None, 0.0, want_T=False)
+    Y_fp = X.double() @ W.double().T                       # unquantized base, fp64 reference
+    nrm = lambda t: float(torch.linalg.vector_norm(t.double()))   # noqa: E731
+    yu = Y_unmerged.double()
+    codes_changed = float((q2.codes != q.codes).double().mean())
+    flop = 2.0 * o * d * r
+    return {
+        "workload": f"merge rank-{r} adapter into the {o}x{d} base, then NF4 + DQ again",
+        "us_merge": round(us_merge, 2), "us_requantize": round(us_requant, 2),
+        "merge_roofline": {"bound": "alu", "achieved": round(flop / (us_merge * 1e-6) / 1e12, 2),
+                           "peak": 157.3, "unit": "TFLOP/s (fp32 FMA)",
+                           "frac": round(flop / (us_merge * 1e-6) / 1e12 / 157.3, 4),
+                           "hbm_GBps": round(o * d * (0.515869 + 4) / (us_merge * 1e-6) / 1e9, 1)},
+        "code_bytes_changed": round(codes_changed, 4),
+        "rel_change_merged_vs_unmerged": nrm(Y_merged.double() - yu) / nrm(yu),
+        "rel_adapter_term": nrm(yu - Y_base.double()) / nrm(yu),
+        "rel_base_quantization_error": nrm(Y_base.double() - Y_fp) / nrm(Y_fp),
+    }
 
 
 def format_errors(qb, torch, W):

@@ -209,6 +209,21 @@ int qlora_linear_fwd_multi(const qlora_bf16* X, int64_t M, int64_t d,
                            const float* s, const int32_t* d_adapter, qlora_bf16* Y,
                            float* T_out, void* ws, size_t ws_bytes, void* stream);
 
+/* Merge an adapter into the base weight, ahead of quantizing the merged layer
+ * again (QLoRA-074 §五, §六: merging and re-quantizing can change outputs;
+ * the weimeta QLoRA glossary FAQ: merge at 16-bit or better, not on the 4-bit
+ * codes):
+ *     W_out[n][k] = fl32( ŵ[n][k] + fl32(s · Δ[k][n]) ),   Δ = A·B,
+ * with Δ accumulated by fp32 fused multiply-adds in increasing j (each bf16
+ * product is exact in fp32, so each step rounds once) and ŵ the fp32
+ * dequantized weight of qlora_dequant.  Pass W_out to qlora_quantize_nf4_dq
+ * to obtain the merged 4-bit layer.
+ *   W      quantized Wq[o][d] (shapes as for qlora_linear_fwd)
+ *   A, B   bf16 [d][r], [r][o]; r == 0 (A, B may be NULL) gives W_out = ŵ
+ *   W_out  device fp32 [o][d], overwritten */
+int qlora_merge_adapter(const qlora_nf4dq* W, int64_t o, int64_t d, const qlora_bf16* A,
+                        const qlora_bf16* B, int64_t r, float s, float* W_out, void* stream);
+
 /* Backward of the QLoRA linear layer (QLoRA-074 §一 and the note on what the
  * backward pass still needs): with U = dY·Bᵀ,
  *     dX = dY·Ŵᵀ + s·U·Aᵀ,   dA = s·Xᵀ·U,   dB = s·Tᵀ·dY,   T = X·A.

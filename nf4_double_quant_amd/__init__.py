@@ -8,7 +8,7 @@ built, or a tensor is not on a HIP device, the calls raise.
 Functions carry the C names:
   qlora_quant_sizes, qlora_codebook, qlora_workspace_bytes,
   qlora_quantize_nf4_dq, qlora_dequant, qlora_linear_fwd, qlora_linear_bwd,
-  qlora_linear_fwd_multi.
+  qlora_linear_fwd_multi, qlora_merge_adapter.
 """
 
 from __future__ import annotations
@@ -64,12 +64,14 @@ def lib() -> ctypes.CDLL:
                                    vp, vp, vp, sz, vp]
     L.qlora_linear_bwd.argtypes = [vp, vp, vp, i64, i64, P(_NF4DQ), i64, vp, vp, i64,
                                    ctypes.c_float, vp, vp, vp, vp, sz, vp]
+    L.qlora_merge_adapter.argtypes = [P(_NF4DQ), i64, i64, vp, vp, i64, ctypes.c_float, vp, vp]
     L.qlora_linear_fwd_multi.argtypes = [vp, i64, i64, P(_NF4DQ), i64, vp, vp, i64, i64,
                                          P(ctypes.c_float), vp, vp, vp, vp, sz, vp]
     L.qlora_timing_begin.argtypes = [ctypes.c_uint32]
     L.qlora_timing_read.argtypes = [i32, P(ctypes.c_double), P(i64)]
     for name in ("qlora_quant_sizes", "qlora_codebook", "qlora_quantize_nf4_dq", "qlora_dequant",
                  "qlora_linear_fwd", "qlora_linear_bwd", "qlora_linear_fwd_multi",
+                 "qlora_merge_adapter",
                  "qlora_timing_begin", "qlora_timing_end",
                  "qlora_timing_read"):
         getattr(L, name).restype = ctypes.c_int
@@ -331,3 +333,17 @@ def qlora_linear_fwd_multi(X, q: QuantizedWeight, A, B, s, adapter, want_T: bool
                                         n, r, s_arr, _ptr(adapter), _ptr(Y), _ptr(T), _ptr(buf),
                                         buf.numel(), _stream(X.device)), "qlora_linear_fwd_multi")
     return Y, T
+
+
+def qlora_merge_adapter(q: QuantizedWeight, A, B, s: float, out=None):
+    """fp32 [o][d] merged weight ŵ + s·(A·B)ᵀ, ready for qlora_quantize_nf4_dq."""
+    torch = _torch()
+    o, d = q.shape
+    r = 0 if A is None else A.shape[1]
+    for t, nm in ((A, "A"), (B, "B")):
+        _need(t, torch.bfloat16, nm, q.device)
+    W = torch.empty((o, d), dtype=torch.float32, device=q.device) if out is None else out
+    _need(W, torch.float32, "out", q.device)
+    _check(lib().qlora_merge_adapter(ctypes.byref(q.view()), o, d, _ptr(A), _ptr(B), r, float(s),
+                                     _ptr(W), _stream(q.device)), "qlora_merge_adapter")
+    return W

@@ -297,6 +297,20 @@ int qlora_linear_fwd_multi(const qlora_bf16* X, int64_t M, int64_t d, const qlor
   return QLORA_OK;
 }
 
+int qlora_merge_adapter(const qlora_nf4dq* W, int64_t o, int64_t d, const qlora_bf16* A,
+                        const qlora_bf16* B, int64_t r, float s, float* W_out, void* stream) {
+  int st = check_linear_shapes(1, d, o, r, W);
+  if (st) return st;
+  if (W_out == nullptr || (r > 0 && (A == nullptr || B == nullptr))) return QLORA_E_INVALID;
+  if (!aligned16(A) || !aligned16(B) || !aligned16(W_out)) return QLORA_E_ALIGN;
+  if ((st = device_status())) return st;
+  hipStream_t hs = (hipStream_t)stream;
+  QL_RUN(QLORA_K_DEQUANT, hs,
+         launch_merge(W->codes, W->scale8, W->scale2, o, d, A, B, (int)r, s, W_out,
+                      host_codebook(W->fmt), hs));
+  return QLORA_OK;
+}
+
 int qlora_linear_bwd(const qlora_bf16* dY, const qlora_bf16* X, const float* T, int64_t M, int64_t d,
                      const qlora_nf4dq* W, int64_t o, const qlora_bf16* A, const qlora_bf16* B,
                      int64_t r, float s, qlora_bf16* dX, qlora_bf16* dA, qlora_bf16* dB, void* ws,

@@ -61,4 +61,10 @@ hipError_t launch_gemv_fwd(const uint16_t* X, int M, int64_t d, const uint8_t* c
                            const int32_t* adapter = nullptr, int n_ad = 0,
                            const float* s_ad = nullptr);
 
+// Adapter merge: W_out[n][k] = fl32(ŵ[n][k] + fl32(s·Σ_j A[k][j]·B[j][n])),
+// the rank sum by fp32 FMAs in increasing j.  d % 64 == 0, o % 8 == 0.
+hipError_t launch_merge(const uint8_t* codes, const uint8_t* scale8, const float* scale2,
+                        int64_t o, int64_t d, const uint16_t* A, const uint16_t* B, int r, float s,
+                        float* W_out, const Codebook& cb, hipStream_t st);
+
 }  // namespace qlora

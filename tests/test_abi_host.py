@@ -157,6 +157,16 @@ def test_multi_adapter_validation(L):
     assert call(view=_view(128 * 128, fmt=9)) == 1
 
 
+def test_merge_validation(L):
+    f = L.qlora_merge_adapter
+    v = _view(128 * 128)
+    assert f(ctypes.byref(v), 128, 128, A16, A16, 16, 2.0, None, None) == 1      # no output
+    assert f(ctypes.byref(v), 128, 128, None, A16, 16, 2.0, A16, None) == 1      # adapter missing
+    assert f(ctypes.byref(v), 128, 100, A16, A16, 16, 2.0, A16, None) == 2       # d % 64
+    assert f(ctypes.byref(v), 128, 128, A16, A16, 12, 2.0, A16, None) == 2       # r % 8
+    assert f(ctypes.byref(v), 128, 128, A16, A16, 16, 2.0, A16 + 4, None) == 3   # alignment
+
+
 def test_no_device_status(L):
     import torch
     if torch.cuda.is_available():
