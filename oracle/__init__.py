@@ -35,6 +35,7 @@ Modules:
   formats -- the int4 / FP4 comparison tables through the same scheme.
   multi   -- one base with a LoRA adapter chosen per token.
   merge   -- the adapter merged into the base, then quantized again.
+  adamw   -- the (paged) optimizer step of the adapter parameters.
 """
 
-from . import nf4, linear, formats, multi, merge  # noqa: F401
+from . import nf4, linear, formats, multi, merge, adamw  # noqa: F401
