@@ -244,6 +244,7 @@ def main():
     decode = None if args.no_decode else bench_decode(args, qb, torch, np, synth, dev)
     formats = format_errors(qb, torch, W)
     merge_res = merge_study(qb, torch, W, q, X, A, B, s)
+    optim = optimizer_study(qb, torch, synth, dev)
     cpu = None if args.no_cpu_baseline else cpu_baseline(args, wl, p)
 
     out = {
@@ -260,7 +261,7 @@ def main():
                    "parallelism": "single GPU"},
         "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "roofline": roofline, "breakdown": breakdown, "decode": decode, "formats": formats,
-        "merge": merge_res,
+        "merge": merge_res, "optimizer": optim,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
@@ -391,6 +392,53 @@ def bench_decode(args, qb, torch, np, synth, dev):
     return {"workload": "decode_mlp_7b: gate/up 4096->11008, down 11008->4096, r=16, fwd only; "
                         "M16_16_adapters: one adapter per token (16 adapters per projection)",
             "weight_sets_cycled": len(sets), "peak_GBps": PEAK_HBM_GBPS, **res}
+
+
+def optimizer_study(qb, torch, synth, dev):
+    """AdamW over the rank-64 adapters of one 65B-style block (7 projections),
+    states in HBM, then paged from pinned host memory through a 64 MiB pool."""
+    wl = synth.WORKLOADS["block_65b"]
+    n = sum(wl.r * (p.d + p.o) for p in wl.projs)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    p = torch.empty(n, device=dev).normal_(0.0, 0.02, generator=gen)
+    g = torch.empty(n, device=dev).normal_(0.0, 1e-3, generator=gen).to(torch.bfloat16)
+    p16 = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    m = torch.zeros(n, device=dev)
+    v = torch.zeros(n, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, reps):
+        fn(1)
+        torch.cuda.synchronize()
+        e0.record()
+        for t in range(reps):
+            fn(t + 2)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    us_dev = timed(lambda t: qb.qlora_adamw_step(p, p16, g, m, v, t), 20)
+    mh, vh = qb.pinned_state(n), qb.pinned_state(n)
+    pool = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
+    us_paged = timed(lambda t: qb.qlora_paged_adamw_step(p, p16, g, mh, vh, t, pool), 5)
+    # host-link reference: plain pinned copies of the same state bytes, each way
+    hbuf = torch.empty(2 * n, dtype=torch.float32, pin_memory=True)
+    dbuf = torch.empty(2 * n, dtype=torch.float32, device=dev)
+    us_h2d = timed(lambda t: dbuf.copy_(hbuf, non_blocking=True), 5)
+    us_d2h = timed(lambda t: hbuf.copy_(dbuf, non_blocking=True), 5)
+    st_bytes = 8 * n                                   # m and v, fp32, one way
+    return {
+        "workload": f"AdamW on the rank-{wl.r} adapters of one 65B-style block: {n} fp32 parameters",
+        "device_states": {"us_per_step": round(us_dev, 2), "bytes_per_param": 28,
+                          "GBps": round(28 * n / (us_dev * 1e-6) / 1e9, 1),
+                          "frac_of_hbm": round(28 * n / (us_dev * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)},
+        "paged_states": {"us_per_step": round(us_paged, 2), "pool_MiB": 64,
+                         "host_link_GBps_each_way": round(st_bytes / (us_paged * 1e-6) / 1e9, 1),
+                         "copy_reference_us": {"h2d": round(us_h2d, 1), "d2h": round(us_d2h, 1)},
+                         "frac_of_sequential_copies": round((us_h2d + us_d2h) / us_paged, 3)},
+        "device_state_bytes_saved": 8 * n,
+    }
 
 
 def merge_study(qb, torch, W, q, X, A, B, s):

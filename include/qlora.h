@@ -224,6 +224,43 @@ int qlora_linear_fwd_multi(const qlora_bf16* X, int64_t M, int64_t d,
 int qlora_merge_adapter(const qlora_nf4dq* W, int64_t o, int64_t d, const qlora_bf16* A,
                         const qlora_bf16* B, int64_t r, float s, float* W_out, void* stream);
 
+/* AdamW hyper-parameters of one step; step is t >= 1, the step being taken. */
+typedef struct qlora_adamw {
+  float lr, beta1, beta2, eps, weight_decay;
+  int64_t step;
+} qlora_adamw;
+
+/* AdamW step of adapter parameters (QLoRA-074 §三: only the LoRA parameters
+ * are updated).  Per element, each operation rounded to fp32 in this order
+ * (sqrt and division correctly rounded, no contraction):
+ *     m' = b1·m + c1·g,  v' = b2·v + c2·(g·g),  den = sqrt(v')·rs + eps,
+ *     p' = p·keep − (lr1·m')/den
+ * with c1 = 1−b1, c2 = 1−b2, rs = 1/sqrt(1−b2^t), keep = 1 − lr·wd and
+ * lr1 = lr/(1−b1^t) formed in fp64 from the fp32 fields (b^t as t products)
+ * and rounded once to fp32.
+ *   p    device fp32[n] master parameters (updated in place)
+ *   p16  device bf16[n] or NULL: receives RNE_bf16(p'), the copy the layer uses
+ *   g    device bf16[n] gradient (dA or dB of qlora_linear_bwd)
+ *   m, v device fp32[n] states (updated in place)
+ * All pointers 16-byte aligned; n >= 0; h->step >= 1. */
+int qlora_adamw_step(float* p, qlora_bf16* p16, const qlora_bf16* g, float* m, float* v,
+                     int64_t n, const qlora_adamw* h, void* stream);
+
+/* The same update with the optimizer states in host memory, paged through a
+ * small device pool (QLoRA-074 §二 and the weimeta QLoRA glossary: the paged
+ * optimizer keeps Adam's states in CPU memory and moves them to the GPU when
+ * the update needs them).  m_host and v_host are pinned host memory
+ * (hipHostMalloc); pool is device memory of pool_bytes >= 8192 split into four
+ * slots of an m page and a v page.  One library copy stream moves pages in
+ * while slots are free, `stream` updates each page, a second copy stream
+ * moves it back out; `stream` waits for the last page, so later work on it
+ * sees the new p, and a host synchronize of it makes m_host and v_host
+ * current.  Results are bitwise those of
+ * qlora_adamw_step.  Not for HIP-graph capture (it uses two more streams). */
+int qlora_paged_adamw_step(float* p, qlora_bf16* p16, const qlora_bf16* g, float* m_host,
+                           float* v_host, int64_t n, const qlora_adamw* h, void* pool,
+                           size_t pool_bytes, void* stream);
+
 /* Backward of the QLoRA linear layer (QLoRA-074 §一 and the note on what the
  * backward pass still needs): with U = dY·Bᵀ,
  *     dX = dY·Ŵᵀ + s·U·Aᵀ,   dA = s·Xᵀ·U,   dB = s·Tᵀ·dY,   T = X·A.

@@ -8,7 +8,8 @@ built, or a tensor is not on a HIP device, the calls raise.
 Functions carry the C names:
   qlora_quant_sizes, qlora_codebook, qlora_workspace_bytes,
   qlora_quantize_nf4_dq, qlora_dequant, qlora_linear_fwd, qlora_linear_bwd,
-  qlora_linear_fwd_multi, qlora_merge_adapter.
+  qlora_linear_fwd_multi, qlora_merge_adapter, qlora_adamw_step,
+  qlora_paged_adamw_step.
 """
 
 from __future__ import annotations
@@ -33,6 +34,11 @@ class QloraError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
         super().__init__(f"{where}: {strerror(status)} (status {status})")
+
+
+class _AdamW(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float), ("step", ctypes.c_int64)]
 
 
 class _NF4DQ(ctypes.Structure):
@@ -64,6 +70,8 @@ def lib() -> ctypes.CDLL:
                                    vp, vp, vp, sz, vp]
     L.qlora_linear_bwd.argtypes = [vp, vp, vp, i64, i64, P(_NF4DQ), i64, vp, vp, i64,
                                    ctypes.c_float, vp, vp, vp, vp, sz, vp]
+    L.qlora_adamw_step.argtypes = [vp, vp, vp, vp, vp, i64, P(_AdamW), vp]
+    L.qlora_paged_adamw_step.argtypes = [vp, vp, vp, vp, vp, i64, P(_AdamW), vp, sz, vp]
     L.qlora_merge_adapter.argtypes = [P(_NF4DQ), i64, i64, vp, vp, i64, ctypes.c_float, vp, vp]
     L.qlora_linear_fwd_multi.argtypes = [vp, i64, i64, P(_NF4DQ), i64, vp, vp, i64, i64,
                                          P(ctypes.c_float), vp, vp, vp, vp, sz, vp]
@@ -71,7 +79,7 @@ def lib() -> ctypes.CDLL:
     L.qlora_timing_read.argtypes = [i32, P(ctypes.c_double), P(i64)]
     for name in ("qlora_quant_sizes", "qlora_codebook", "qlora_quantize_nf4_dq", "qlora_dequant",
                  "qlora_linear_fwd", "qlora_linear_bwd", "qlora_linear_fwd_multi",
-                 "qlora_merge_adapter",
+                 "qlora_merge_adapter", "qlora_adamw_step", "qlora_paged_adamw_step",
                  "qlora_timing_begin", "qlora_timing_end",
                  "qlora_timing_read"):
         getattr(L, name).restype = ctypes.c_int
@@ -347,3 +355,46 @@ def qlora_merge_adapter(q: QuantizedWeight, A, B, s: float, out=None):
     _check(lib().qlora_merge_adapter(ctypes.byref(q.view()), o, d, _ptr(A), _ptr(B), r, float(s),
                                      _ptr(W), _stream(q.device)), "qlora_merge_adapter")
     return W
+
+
+def _adamw(step, lr, beta1, beta2, eps, weight_decay):
+    return _AdamW(float(lr), float(beta1), float(beta2), float(eps), float(weight_decay), int(step))
+
+
+def qlora_adamw_step(p, p16, g, m, v, step, lr=1e-4, beta1=0.9, beta2=0.999, eps=1e-8,
+                     weight_decay=0.0):
+    """AdamW on device tensors: p, m, v fp32 (in place), g bf16, p16 bf16 or None."""
+    torch = _torch()
+    _need(p, torch.float32, "p")
+    for t, nm, dt in ((m, "m", torch.float32), (v, "v", torch.float32), (g, "g", torch.bfloat16),
+                      (p16, "p16", torch.bfloat16)):
+        _need(t, dt, nm, p.device)
+    n = p.numel()
+    h = _adamw(step, lr, beta1, beta2, eps, weight_decay)
+    _check(lib().qlora_adamw_step(_ptr(p), _ptr(p16), _ptr(g), _ptr(m), _ptr(v), n, ctypes.byref(h),
+                                  _stream(p.device)), "qlora_adamw_step")
+
+
+def pinned_state(n, device=None):
+    """A pinned host fp32 buffer for the paged optimizer states (zeros)."""
+    torch = _torch()
+    return torch.zeros(n, dtype=torch.float32, pin_memory=True)
+
+
+def qlora_paged_adamw_step(p, p16, g, m_host, v_host, step, pool, lr=1e-4, beta1=0.9,
+                           beta2=0.999, eps=1e-8, weight_decay=0.0):
+    """AdamW with the states in pinned host tensors, paged through `pool` (a
+    device uint8 tensor of at least 4096 bytes)."""
+    torch = _torch()
+    _need(p, torch.float32, "p")
+    for t, nm, dt in ((g, "g", torch.bfloat16), (p16, "p16", torch.bfloat16),
+                      (pool, "pool", torch.uint8)):
+        _need(t, dt, nm, p.device)
+    for t, nm in ((m_host, "m_host"), (v_host, "v_host")):
+        if t.device.type != "cpu" or not t.is_pinned() or t.dtype != torch.float32:
+            raise TypeError(f"{nm} must be a pinned host fp32 tensor")
+    n = p.numel()
+    h = _adamw(step, lr, beta1, beta2, eps, weight_decay)
+    _check(lib().qlora_paged_adamw_step(_ptr(p), _ptr(p16), _ptr(g), _ptr(m_host), _ptr(v_host), n,
+                                        ctypes.byref(h), _ptr(pool), pool.numel(), _stream(p.device)),
+           "qlora_paged_adamw_step")

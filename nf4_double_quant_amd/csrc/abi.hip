@@ -311,6 +311,44 @@ int qlora_merge_adapter(const qlora_nf4dq* W, int64_t o, int64_t d, const qlora_
   return QLORA_OK;
 }
 
+namespace {
+int check_adamw(const float* p, const qlora_bf16* p16, const qlora_bf16* g, const float* m,
+                const float* v, int64_t n, const qlora_adamw* h) {
+  if (h == nullptr || n < 0 || h->step < 1) return QLORA_E_INVALID;
+  if (n > 0 && (p == nullptr || g == nullptr || m == nullptr || v == nullptr)) return QLORA_E_INVALID;
+  if (!aligned16(p) || !aligned16(p16) || !aligned16(g) || !aligned16(m) || !aligned16(v))
+    return QLORA_E_ALIGN;
+  return QLORA_OK;
+}
+}  // namespace
+
+int qlora_adamw_step(float* p, qlora_bf16* p16, const qlora_bf16* g, float* m, float* v,
+                     int64_t n, const qlora_adamw* h, void* stream) {
+  int st = check_adamw(p, p16, g, m, v, n, h);
+  if (st) return st;
+  if (n == 0) return QLORA_OK;
+  if ((st = device_status())) return st;
+  const AdamwConsts k = adamw_consts(h->lr, h->beta1, h->beta2, h->eps, h->weight_decay, h->step);
+  QL_RUN(QLORA_K_GRADS, (hipStream_t)stream, launch_adamw(p, p16, g, m, v, n, k, (hipStream_t)stream));
+  return QLORA_OK;
+}
+
+int qlora_paged_adamw_step(float* p, qlora_bf16* p16, const qlora_bf16* g, float* m_host,
+                           float* v_host, int64_t n, const qlora_adamw* h, void* pool,
+                           size_t pool_bytes, void* stream) {
+  int st = check_adamw(p, p16, g, m_host, v_host, n, h);
+  if (st) return st;
+  if (!aligned16(pool)) return QLORA_E_ALIGN;
+  if (n > 0 && (pool == nullptr || paged_adamw_page_elems(pool_bytes) <= 0)) return QLORA_E_WORKSPACE;
+  if (n == 0) return QLORA_OK;
+  if ((st = device_status())) return st;
+  const AdamwConsts k = adamw_consts(h->lr, h->beta1, h->beta2, h->eps, h->weight_decay, h->step);
+  if (launch_paged_adamw(p, p16, g, m_host, v_host, n, k, pool, pool_bytes, (hipStream_t)stream) !=
+      hipSuccess)
+    return QLORA_E_HIP;
+  return QLORA_OK;
+}
+
 int qlora_linear_bwd(const qlora_bf16* dY, const qlora_bf16* X, const float* T, int64_t M, int64_t d,
                      const qlora_nf4dq* W, int64_t o, const qlora_bf16* A, const qlora_bf16* B,
                      int64_t r, float s, qlora_bf16* dX, qlora_bf16* dA, qlora_bf16* dB, void* ws,

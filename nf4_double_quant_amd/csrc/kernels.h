@@ -67,4 +67,16 @@ hipError_t launch_merge(const uint8_t* codes, const uint8_t* scale8, const float
                         int64_t o, int64_t d, const uint16_t* A, const uint16_t* B, int r, float s,
                         float* W_out, const Codebook& cb, hipStream_t st);
 
+// AdamW of the adapter parameters (optim.hip).
+struct AdamwConsts {
+  float b1, b2, c1, c2, rs, keep, lr1, eps;
+};
+AdamwConsts adamw_consts(float lr, float b1, float b2, float eps, float wd, int64_t t);
+hipError_t launch_adamw(float* p, uint16_t* p16, const uint16_t* g, float* m, float* v, int64_t n,
+                        const AdamwConsts& k, hipStream_t st);
+int64_t paged_adamw_page_elems(size_t pool_bytes);
+hipError_t launch_paged_adamw(float* p, uint16_t* p16, const uint16_t* g, float* m_host,
+                              float* v_host, int64_t n, const AdamwConsts& k, void* pool,
+                              size_t pool_bytes, hipStream_t st);
+
 }  // namespace qlora

@@ -167,6 +167,19 @@ def test_merge_validation(L):
     assert f(ctypes.byref(v), 128, 128, A16, A16, 16, 2.0, A16 + 4, None) == 3   # alignment
 
 
+def test_adamw_validation(L):
+    h = qb._adamw(1, 1e-4, 0.9, 0.999, 1e-8, 0.0)
+    h0 = qb._adamw(0, 1e-4, 0.9, 0.999, 1e-8, 0.0)
+    f, fp = L.qlora_adamw_step, L.qlora_paged_adamw_step
+    assert f(A16, None, A16, A16, A16, 100, None, None) == 1            # no hyper-parameters
+    assert f(A16, None, A16, A16, A16, 100, ctypes.byref(h0), None) == 1  # step must be >= 1
+    assert f(None, None, A16, A16, A16, 100, ctypes.byref(h), None) == 1
+    assert f(A16 + 4, None, A16, A16, A16, 100, ctypes.byref(h), None) == 3
+    assert f(A16, None, A16, A16, A16, 0, ctypes.byref(h), None) == 0     # n = 0: no-op
+    assert fp(A16, None, A16, A16, A16, 100, ctypes.byref(h), A16, 4096, None) == 4   # pool too small
+    assert fp(A16, None, A16, A16, A16, 100, ctypes.byref(h), None, 1 << 20, None) == 4
+
+
 def test_no_device_status(L):
     import torch
     if torch.cuda.is_available():
