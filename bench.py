@@ -33,7 +33,8 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
 PROFILE_PMC = os.path.join(ROOT, "profiles", "pmc_main_gemm_linear_4096.json")
-KERNEL_SOURCES = ["qgemm.hip", "kernels.h", "common.h"]
+# the sources that define k_qgemm's code (kernels.h only declares launchers)
+KERNEL_SOURCES = ["qgemm.hip", "common.h"]
 
 
 def parse():
