@@ -33,9 +33,10 @@ Modules:
   nf4     -- codebook, blockwise NF4 encode, double quantization, dequant.
   linear  -- forward / backward of Y = X·Ŵ + s·X·A·B in fp64.
   formats -- the int4 / FP4 comparison tables through the same scheme.
+  dq      -- second-level variants centred on the tensor mean (int8, FP8).
   multi   -- one base with a LoRA adapter chosen per token.
   merge   -- the adapter merged into the base, then quantized again.
   adamw   -- the (paged) optimizer step of the adapter parameters.
 """
 
-from . import nf4, linear, formats, multi, merge, adamw  # noqa: F401
+from . import nf4, linear, formats, dq, multi, merge, adamw  # noqa: F401
