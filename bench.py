@@ -13,8 +13,9 @@ s = 2, W ~ N(0, 0.02), X, dY ~ N(0, 1), A, B ~ N(0, 0.02).
 (quantize and dequant count no FLOPs; their time is included).  The JSON line
 also carries the dominant kernel's roofline, the few-token dequant-GEMV
 bandwidth on the 7B-style MLP weights, the quantization error of each 4-bit
-table (NF4, int4, FP4 E2M1, FP4 E3M0) on the workload's weight, and the CPU
-oracle timed on the host.
+table (NF4, int4, FP4 E2M1, FP4 E3M0) and of the second-level variants on the
+workload's weight, the merge/re-quantize study, the (paged) AdamW step of a
+65B-style block's adapters, and the CPU oracle timed on the host.
 """
 
 from __future__ import annotations
@@ -496,7 +497,12 @@ def format_errors(qb, torch, W):
     for fmt in qb.FORMATS:
         q = qb.qlora_quantize_nf4_dq(W, check_finite=False, fmt=fmt)
         mse = float(((qb.qlora_dequant(q).double() - W.double()) ** 2).mean())
-        out[fmt] = {"mse": mse, "mse_over_var": round(mse / var, 5)}
+        out[fmt] = {"mse": mse, "mse_over_var": round(mse / var, 6)}
+    # the second-level variants centred on the tensor mean, with NF4 codes
+    for v in ("int8_mean", "fp8_mean"):
+        q = qb.qlora_quantize_nf4_dq(W, check_finite=False, dq=v)
+        mse = float(((qb.qlora_dequant(q).double() - W.double()) ** 2).mean())
+        out["nf4+" + v] = {"mse": mse, "mse_over_var": round(mse / var, 6)}
     return out
 
 

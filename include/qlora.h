@@ -98,17 +98,35 @@ typedef enum {
   QLORA_FMT_FP4_E3M0 = 3
 } qlora_fmt;
 
+/* The code of the first-level constants (the double quantization).  UINT8 is
+ * this library's reading of the method (QLoRA-074 §二: 8-bit constants, one
+ * fp32 per 256): an unsigned linear code with no offset.  The variants centre
+ * the constants on their tensor mean first (the page notes that offsets
+ * exist beside the 8-bit constants) and code them as symmetric int8 or as
+ * FP8 E4M3; scale2 then holds the steps followed by the mean.  Only the
+ * quantizer with a workspace (qlora_quantize_nf4_dq_ws) and qlora_dequant
+ * accept the variants. */
+typedef enum {
+  QLORA_DQ_UINT8 = 0,
+  QLORA_DQ_INT8_MEAN = 1,
+  QLORA_DQ_FP8_MEAN = 2
+} qlora_dq;
+
 /* Non-owning view of a quantized tensor (QLoRA-074 §三: the frozen W4 codes
  * plus the 8-bit first-level and fp32 second-level constants).  All three
- * buffers are device memory sized by qlora_quant_sizes(n).  fmt selects the
- * table of the codes (0 = NF4, so a zero-initialised view is NF4); an
- * unknown fmt makes every entry point return QLORA_E_INVALID. */
+ * buffers are device memory sized by qlora_quant_sizes(n) (qlora_quant_sizes_dq
+ * for a dq variant).  fmt selects the table of the codes and dq the code of
+ * the constants (0 = NF4 and UINT8, so a zero-initialised view is the
+ * default); unknown values make every entry point return QLORA_E_INVALID,
+ * and so does a dq variant passed to an entry point other than
+ * qlora_quantize_nf4_dq_ws and qlora_dequant. */
 typedef struct qlora_nf4dq {
   uint8_t* codes;   /* 4*ceil(n/8) bytes      */
   uint8_t* scale8;  /* ceil(n/64) bytes       */
   float* scale2;    /* ceil(n/16384) floats   */
   int64_t n;        /* number of weights      */
   int32_t fmt;      /* a qlora_fmt            */
+  int32_t dq;       /* a qlora_dq             */
 } qlora_nf4dq;
 
 /* ---------------------------------------------------------------- host helpers */
@@ -130,6 +148,13 @@ int qlora_quant_sizes(int64_t n, int64_t* codes_bytes, int64_t* scale8_bytes,
  * exponent bits, field 0 = zero, field e = 2^(e−7).  Both FP4 tables keep −0
  * (index 7) and +0 (index 8). */
 int qlora_codebook(int fmt, float* out);
+
+/* Sizes for second-level variant dq: scale2 gains one float (the tensor mean)
+ * when dq != QLORA_DQ_UINT8, and *ws_bytes is the workspace of
+ * qlora_quantize_nf4_dq_ws (8 bytes per 16384-weight group).  Any output
+ * pointer may be NULL.  Pure host code. */
+int qlora_quant_sizes_dq(int64_t n, int dq, int64_t* codes_bytes, int64_t* scale8_bytes,
+                         int64_t* scale2_bytes, int64_t* ws_bytes);
 
 /* Workspace in bytes needed by qlora_linear_fwd (op = QLORA_OP_FWD) or
  * qlora_linear_bwd (op = QLORA_OP_BWD) for these sizes.  Returns 0 for
@@ -155,16 +180,32 @@ const char* qlora_version(void);
  * strictly below w/c1 (exact comparison): the nearest value, ties to the
  * lower index (with the duplicated zero of the FP4 tables a weight rounding
  * to zero keeps its sign, +0 only for w > 0); a zero block gets code 7.
- * The table is out->fmt; codes past n are 7 for every table.  Per group:
+ * The table is out->fmt (out->dq must be QLORA_DQ_UINT8; the variants need
+ * qlora_quantize_nf4_dq_ws); codes past n are 7 for every table.  Per group:
  * step = fl32(max c1 / 255); q = the integer in 0..255 nearest to c1/step
  * (ties to the lower), 0 if step is 0. */
 int qlora_quantize_nf4_dq(const float* W, int64_t n, const qlora_nf4dq* out,
                           int32_t* d_flags, void* stream);
 
+/* The quantizer for any second-level variant out->dq (QLORA_DQ_UINT8 gives
+ * exactly qlora_quantize_nf4_dq).  The codes are those of the default scheme
+ * (encoded with the exact c1).  For the variants, per tensor:
+ * μ = fl32(S/nb), S the fp64 sum of the block constants c1 (each group in
+ * block order, then the groups in order); per block c' = fl32(c1 − μ); per
+ * group step = fl32(max|c'| / 127) (INT8_MEAN) or fl32(max|c'| / 448)
+ * (FP8_MEAN), 0 if max|c'| = 0; scale8[b] = the nearest int8 (two's
+ * complement, ties to the smaller magnitude) or the nearest E4M3 value
+ * (bias 7, subnormals, ties to the even mantissa, never −0) of c'/step;
+ * scale2 = the steps, then μ.  ĉ = fl32(fl32(q·step) + μ).
+ *   ws  device workspace of qlora_quant_sizes_dq(...)->ws_bytes bytes. */
+int qlora_quantize_nf4_dq_ws(const float* W, int64_t n, const qlora_nf4dq* out,
+                             int32_t* d_flags, void* ws, size_t ws_bytes, void* stream);
+
 /* Dequantization Ŵ = Dequant(W4bit, scales) (QLoRA-074 §一; §三: the
  * weights a product needs are dequantized to BF16 on demand).
  *   q          quantized tensor (device buffers), q->n >= 0.
- *   out_dtype  QLORA_F32: out is fp32[n] with ŵ_i = fl32(V[k]·fl32(q8·step));
+ *   out_dtype  QLORA_F32: out is fp32[n] with ŵ_i = fl32(V[k]·ĉ), ĉ = fl32(q8·step)
+ *              (or the ĉ of the view's dq variant);
  *              QLORA_BF16: out is bf16[n] holding RNE_bf16(ŵ_i).
  * Bit-exact by construction: two IEEE fp32 products, nearest-even rounding. */
 int qlora_dequant(const qlora_nf4dq* q, int out_dtype, void* out, void* stream);

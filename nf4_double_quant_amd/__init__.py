@@ -24,8 +24,9 @@ LIB_PATH = os.path.join(_PKG, "libqlora.so")
 QLORA_OK, QLORA_E_NONFINITE = 0, 7
 QLORA_F32, QLORA_BF16 = 0, 1
 QLORA_OP_FWD, QLORA_OP_BWD = 0, 1
-# Tables of the 4-bit codes (qlora_fmt).
+# Tables of the 4-bit codes (qlora_fmt) and codes of the constants (qlora_dq).
 FORMATS = {"nf4": 0, "int4": 1, "fp4_e2m1": 2, "fp4_e3m0": 3}
+DQ_VARIANTS = {"uint8": 0, "int8_mean": 1, "fp8_mean": 2}
 
 _lib = None
 
@@ -43,7 +44,8 @@ class _AdamW(ctypes.Structure):
 
 class _NF4DQ(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("scale8", ctypes.c_void_p),
-                ("scale2", ctypes.c_void_p), ("n", ctypes.c_int64), ("fmt", ctypes.c_int32)]
+                ("scale2", ctypes.c_void_p), ("n", ctypes.c_int64), ("fmt", ctypes.c_int32),
+                ("dq", ctypes.c_int32)]
 
 
 def lib() -> ctypes.CDLL:
@@ -65,6 +67,8 @@ def lib() -> ctypes.CDLL:
     L.qlora_strerror.restype = ctypes.c_char_p
     L.qlora_version.restype = ctypes.c_char_p
     L.qlora_quantize_nf4_dq.argtypes = [vp, i64, P(_NF4DQ), vp, vp]
+    L.qlora_quantize_nf4_dq_ws.argtypes = [vp, i64, P(_NF4DQ), vp, vp, sz, vp]
+    L.qlora_quant_sizes_dq.argtypes = [i64, i32, P(i64), P(i64), P(i64), P(i64)]
     L.qlora_dequant.argtypes = [P(_NF4DQ), i32, vp, vp]
     L.qlora_linear_fwd.argtypes = [vp, i64, i64, P(_NF4DQ), i64, vp, vp, i64, ctypes.c_float,
                                    vp, vp, vp, sz, vp]
@@ -77,7 +81,8 @@ def lib() -> ctypes.CDLL:
                                          P(ctypes.c_float), vp, vp, vp, vp, sz, vp]
     L.qlora_timing_begin.argtypes = [ctypes.c_uint32]
     L.qlora_timing_read.argtypes = [i32, P(ctypes.c_double), P(i64)]
-    for name in ("qlora_quant_sizes", "qlora_codebook", "qlora_quantize_nf4_dq", "qlora_dequant",
+    for name in ("qlora_quant_sizes", "qlora_quant_sizes_dq", "qlora_quantize_nf4_dq_ws",
+                 "qlora_codebook", "qlora_quantize_nf4_dq", "qlora_dequant",
                  "qlora_linear_fwd", "qlora_linear_bwd", "qlora_linear_fwd_multi",
                  "qlora_merge_adapter", "qlora_adamw_step", "qlora_paged_adamw_step",
                  "qlora_timing_begin", "qlora_timing_end",
@@ -97,6 +102,15 @@ def _check(status: int, where: str):
 
 
 # ------------------------------------------------------------------ host helpers
+
+def qlora_quant_sizes_dq(n: int, dq="uint8") -> tuple[int, int, int, int]:
+    """(codes, scale8, scale2, workspace) bytes for a second-level variant."""
+    c, s8, s2, w = (ctypes.c_int64() for _ in range(4))
+    code = DQ_VARIANTS[dq] if isinstance(dq, str) else int(dq)
+    _check(lib().qlora_quant_sizes_dq(n, code, ctypes.byref(c), ctypes.byref(s8), ctypes.byref(s2),
+                                      ctypes.byref(w)), "qlora_quant_sizes_dq")
+    return c.value, s8.value, s2.value, w.value
+
 
 def qlora_quant_sizes(n: int) -> tuple[int, int, int]:
     c, s8, s2 = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
@@ -187,45 +201,56 @@ class QuantizedWeight:
     n: int
     shape: tuple
     fmt: int = 0
+    dq: int = 0
 
     def view(self) -> _NF4DQ:
         return _NF4DQ(self.codes.data_ptr(), self.scale8.data_ptr(), self.scale2.data_ptr(), self.n,
-                      self.fmt)
+                      self.fmt, self.dq)
 
     @property
     def device(self):
         return self.codes.device
 
 
-def _alloc_quantized(n: int, shape, device, fmt: int) -> QuantizedWeight:
+def _alloc_quantized(n: int, shape, device, fmt: int, dq: int = 0) -> QuantizedWeight:
     torch = _torch()
-    c, s8, s2 = qlora_quant_sizes(n)
+    c, s8, s2, _ = qlora_quant_sizes_dq(n, dq)
     return QuantizedWeight(torch.empty(max(c, 1), dtype=torch.uint8, device=device),
                            torch.empty(max(s8, 1), dtype=torch.uint8, device=device),
                            torch.empty(max(s2 // 4, 1), dtype=torch.float32, device=device),
-                           n, tuple(shape), fmt)
+                           n, tuple(shape), fmt, dq)
 
 
 def qlora_quantize_nf4_dq(W, check_finite: bool = True, out: QuantizedWeight | None = None,
-                          fmt="nf4") -> QuantizedWeight:
+                          fmt="nf4", dq="uint8") -> QuantizedWeight:
     """Blockwise 4-bit + double quantization of an fp32 device tensor (any shape, flattened).
 
-    `fmt` picks the code table (NF4 by default).  `out` reuses the buffers of
-    an earlier result of the same size (and keeps its table).  With
-    check_finite the call waits for the kernel and raises on NaN/Inf input.
+    `fmt` picks the code table (NF4 by default) and `dq` the code of the
+    constants ("uint8" by default, or "int8_mean" / "fp8_mean", which run the
+    workspace quantizer).  `out` reuses the buffers of an earlier result of
+    the same size (and keeps its table and variant).  With check_finite the
+    call waits for the kernel and raises on NaN/Inf input.
     """
     torch = _torch()
     _need(W, torch.float32, "W")
     if out is not None and out.n != W.numel():
         raise ValueError("out holds a different number of weights")
-    q = _alloc_quantized(W.numel(), W.shape, W.device, _fmt_code(fmt)) if out is None else out
+    dq_code = DQ_VARIANTS[dq] if isinstance(dq, str) else int(dq)
+    q = _alloc_quantized(W.numel(), W.shape, W.device, _fmt_code(fmt), dq_code) if out is None else out
     flags = getattr(q, "flags", None)
     if flags is None:
         flags = torch.zeros(1, dtype=torch.int32, device=W.device)
     elif check_finite:
         flags.zero_()
-    _check(lib().qlora_quantize_nf4_dq(_ptr(W), W.numel(), ctypes.byref(q.view()), _ptr(flags),
-                                       _stream(W.device)), "qlora_quantize_nf4_dq")
+    if q.dq == 0:
+        _check(lib().qlora_quantize_nf4_dq(_ptr(W), W.numel(), ctypes.byref(q.view()), _ptr(flags),
+                                           _stream(W.device)), "qlora_quantize_nf4_dq")
+    else:
+        nws = qlora_quant_sizes_dq(W.numel(), q.dq)[3]
+        ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=W.device)
+        _check(lib().qlora_quantize_nf4_dq_ws(_ptr(W), W.numel(), ctypes.byref(q.view()), _ptr(flags),
+                                              _ptr(ws), ws.numel(), _stream(W.device)),
+               "qlora_quantize_nf4_dq_ws")
     if check_finite and int(flags.item()) & 1:
         raise QloraError(QLORA_E_NONFINITE, "qlora_quantize_nf4_dq")
     q.flags = flags

@@ -111,10 +111,15 @@ hipError_t timed(int cls, hipStream_t st, F&& f) {
 // Launch one kernel of class `cls` (timed while diagnostics are on).
 #define QL_RUN(cls, st, expr) QL_TRY(timed((cls), (st), [&]() { return (expr); }))
 
-int check_quant_view(const qlora_nf4dq* q) {
+// allow_dq: whether the entry point decodes the second-level variants (the
+// standalone quantizer and dequantizer); the fused kernels decode only the
+// default one.
+int check_quant_view(const qlora_nf4dq* q, bool allow_dq = false) {
   if (q == nullptr) return QLORA_E_INVALID;
   if (q->n < 0) return QLORA_E_INVALID;
   if (q->fmt < QLORA_FMT_NF4 || q->fmt > QLORA_FMT_FP4_E3M0) return QLORA_E_INVALID;
+  if (q->dq < QLORA_DQ_UINT8 || q->dq > QLORA_DQ_FP8_MEAN) return QLORA_E_INVALID;
+  if (q->dq != QLORA_DQ_UINT8 && !allow_dq) return QLORA_E_INVALID;
   if (q->n > 0 && (q->codes == nullptr || q->scale8 == nullptr || q->scale2 == nullptr))
     return QLORA_E_INVALID;
   if (!aligned16(q->codes) || !aligned16(q->scale8) || !aligned16(q->scale2)) return QLORA_E_ALIGN;
@@ -217,8 +222,42 @@ int qlora_quantize_nf4_dq(const float* W, int64_t n, const qlora_nf4dq* out, int
   return QLORA_OK;
 }
 
+int qlora_quant_sizes_dq(int64_t n, int dq, int64_t* codes_bytes, int64_t* scale8_bytes,
+                         int64_t* scale2_bytes, int64_t* ws_bytes) {
+  if (n < 0 || dq < QLORA_DQ_UINT8 || dq > QLORA_DQ_FP8_MEAN) return QLORA_E_INVALID;
+  int64_t c = 0, s8 = 0, s2 = 0;
+  qlora_quant_sizes(n, &c, &s8, &s2);
+  const int64_t ng = s2 / 4;
+  if (codes_bytes) *codes_bytes = c;
+  if (scale8_bytes) *scale8_bytes = s8;
+  if (scale2_bytes) *scale2_bytes = s2 + (dq != QLORA_DQ_UINT8 && n > 0 ? 4 : 0);
+  if (ws_bytes) *ws_bytes = dq != QLORA_DQ_UINT8 ? up(8 * ng) : 0;
+  return QLORA_OK;
+}
+
+int qlora_quantize_nf4_dq_ws(const float* W, int64_t n, const qlora_nf4dq* out, int32_t* d_flags,
+                             void* ws, size_t ws_bytes, void* stream) {
+  if (n < 0 || out == nullptr) return QLORA_E_INVALID;
+  if (n > 0 && W == nullptr) return QLORA_E_INVALID;
+  int st = check_quant_view(out, true);
+  if (st) return st;
+  if (out->n != n) return QLORA_E_SHAPE;
+  if (!aligned16(W) || !aligned16(ws)) return QLORA_E_ALIGN;
+  int64_t need = 0;
+  qlora_quant_sizes_dq(n, out->dq, nullptr, nullptr, nullptr, &need);
+  if ((int64_t)ws_bytes < need || (need > 0 && ws == nullptr)) return QLORA_E_WORKSPACE;
+  if (n == 0) return QLORA_OK;
+  if ((st = device_status())) return st;
+  hipStream_t hs = (hipStream_t)stream;
+  QL_RUN(QLORA_K_QUANTIZE, hs, launch_quantize(W, n, out->codes, out->scale8, out->scale2, d_flags,
+                                               host_codebook(out->fmt), hs));
+  QL_RUN(QLORA_K_QUANTIZE, hs, launch_dq_variant(W, n, out->scale8, out->scale2, out->dq,
+                                                 static_cast<double*>(ws), hs));
+  return QLORA_OK;
+}
+
 int qlora_dequant(const qlora_nf4dq* q, int out_dtype, void* out, void* stream) {
-  int st = check_quant_view(q);
+  int st = check_quant_view(q, true);
   if (st) return st;
   if (out_dtype != QLORA_F32 && out_dtype != QLORA_BF16) return QLORA_E_INVALID;
   if (q->n > 0 && out == nullptr) return QLORA_E_INVALID;
@@ -226,7 +265,7 @@ int qlora_dequant(const qlora_nf4dq* q, int out_dtype, void* out, void* stream) 
   if (q->n == 0) return QLORA_OK;
   if ((st = device_status())) return st;
   QL_RUN(QLORA_K_DEQUANT, (hipStream_t)stream, launch_dequant(q->codes, q->scale8, q->scale2, q->n, out_dtype == QLORA_BF16, out,
-                        host_codebook(q->fmt), (hipStream_t)stream));
+                        host_codebook(q->fmt), (hipStream_t)stream, q->dq));
   return QLORA_OK;
 }
 

@@ -10,8 +10,15 @@ namespace qlora {
 // cb: the 16-entry table of the codes (host_codebook(fmt)).
 hipError_t launch_quantize(const float* W, int64_t n, uint8_t* codes, uint8_t* scale8,
                            float* scale2, int32_t* flags, const Codebook& cb, hipStream_t st);
+// dq: second-level variant (0 default; 1 int8 around the tensor mean; 2 E4M3
+// around it, the mean stored after the steps in scale2).
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scale8, const float* scale2,
-                          int64_t n, bool bf16, void* out, const Codebook& cb, hipStream_t st);
+                          int64_t n, bool bf16, void* out, const Codebook& cb, hipStream_t st,
+                          int dq = 0);
+// Rewrites scale8 and scale2 (+ the mean) for variant dq after launch_quantize.
+// psum: device workspace of ceil(n/16384) doubles.
+hipError_t launch_dq_variant(const float* W, int64_t n, uint8_t* scale8, float* scale2, int dq,
+                             double* psum, hipStream_t st);
 
 
 // Fused NF4 dequant-GEMM: C = A·Ŵ (+ A2·B2) with Ŵ from the quantized Wq[o][d].

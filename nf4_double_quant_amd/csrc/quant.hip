@@ -197,13 +197,37 @@ __device__ __forceinline__ uint32_t code_of(uint32_t w, int j) {
   return (w >> (8 * (j & 3) + 4 * (j >> 2))) & 15u;
 }
 
-// Eight weights per thread (one code word); ŵ = fl32(V[k]·fl32(q8·step)).
+// E4M3 value of an 8-bit pattern (bias 7, subnormals; 0x7F/0xFF never
+// produced by the encoder).
+__device__ __forceinline__ float e4m3_value(uint32_t q) {
+  const int e = (int)((q >> 3) & 15), m = (int)(q & 7);
+  const float mag = e == 0 ? ldexpf((float)m, -9) : ldexpf((float)(8 + m), e - 10);
+  return (q & 0x80) ? -mag : mag;
+}
+
+// ĉ of block b for the second-level variant dq (0: q8·step; 1: int8 around
+// the tensor mean μ; 2: E4M3 around μ), each operation rounded to fp32.
+__device__ __forceinline__ float block_chat(const uint8_t* scale8, const float* scale2, int64_t b,
+                                            int dq, float mu) {
+#pragma clang fp contract(off)
+  const uint32_t q = scale8[b];
+  const float step = scale2[b / kGroup];
+  if (dq == 0) return (float)q * step;
+  const float qv = dq == 1 ? (float)(int8_t)q : e4m3_value(q);
+  return qv * step + mu;
+}
+
+// Eight weights per thread (one code word); ŵ = fl32(V[k]·ĉ) with ĉ of the
+// block's second-level variant (fl32(q8·step) by default).
 template <bool kBf16>
 __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ codes,
                                                  const uint8_t* __restrict__ scale8,
                                                  const float* __restrict__ scale2, int64_t n,
-                                                 void* __restrict__ out, Codebook cb) {
+                                                 void* __restrict__ out, Codebook cb, int dq) {
+#pragma clang fp contract(off)
   __shared__ float s_v[16];
+  const int64_t ngr = ((n + kBlock - 1) / kBlock + kGroup - 1) / kGroup;
+  const float mu = dq != 0 ? scale2[ngr] : 0.0f;
   if (threadIdx.x < 16) s_v[threadIdx.x] = cb.v[threadIdx.x];
   __syncthreads();
   const int64_t n8 = (n + 7) / 8;
@@ -211,7 +235,7 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ cod
        i += (int64_t)gridDim.x * blockDim.x) {
     const int64_t e0 = i * 8;
     const int64_t b = e0 / kBlock;
-    const float chat = (float)scale8[b] * scale2[b / kGroup];
+    const float chat = block_chat(scale8, scale2, b, dq, mu);
     const uint32_t w = reinterpret_cast<const uint32_t*>(codes)[i];
     float r[8];
 #pragma unroll
@@ -242,6 +266,111 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ cod
   }
 }
 
+// ------------------------------------------------------------------ second-level variants
+// The constants centred on the tensor mean μ before their 8-bit code (the
+// offset the QLoRA page mentions beside the 8-bit constants; int8 or E4M3
+// codes).  Three launches after k_quantize has written the codes: per-group
+// sums of c1, the mean, then each group's new step and codes.  The sums and
+// the mean use fixed orders, so the results are reproducible bit for bit.
+
+// c1 of block b (valid weights only), as k_quantize computes it.
+__device__ __forceinline__ float dq_block_c1(const float* W, int64_t n, int64_t b) {
+  const int64_t e0 = b * kBlock;
+  uint32_t m = 0;
+  for (int k = 0; k < kBlock; ++k)
+    if (e0 + k < n) m = max(m, abs_bits(W[e0 + k]));
+  return __uint_as_float(m);
+}
+
+__global__ __launch_bounds__(256) void k_dq_psum(const float* __restrict__ W, int64_t n,
+                                                 double* __restrict__ psum) {
+  __shared__ float s_c1[kGroup];
+  const int64_t nb = (n + kBlock - 1) / kBlock;
+  const int64_t b = (int64_t)blockIdx.x * kGroup + threadIdx.x;
+  s_c1[threadIdx.x] = b < nb ? dq_block_c1(W, n, b) : 0.0f;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double sum = 0.0;
+    for (int i = 0; i < kGroup; ++i) sum += (double)s_c1[i];   // increasing block order
+    psum[blockIdx.x] = sum;
+  }
+}
+
+__global__ void k_dq_mean(const double* __restrict__ psum, int64_t ng, int64_t nb,
+                          float* __restrict__ scale2) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  double tot = 0.0;
+  for (int64_t g = 0; g < ng; ++g) tot += psum[g];              // increasing group order
+  scale2[ng] = (float)(tot / (double)nb);
+}
+
+// Largest E4M3 value of a 7-bit magnitude code, as fp64.
+__device__ __forceinline__ double e4m3_mag(int code) {
+  const int e = code >> 3, m = code & 7;
+  return e == 0 ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
+}
+
+__global__ __launch_bounds__(256) void k_dq_second(const float* __restrict__ W, int64_t n,
+                                                   uint8_t* __restrict__ scale8,
+                                                   float* __restrict__ scale2, int dq) {
+#pragma clang fp contract(off)
+  __shared__ uint32_t s_red[4];
+  const int t = threadIdx.x;
+  const int64_t nb = (n + kBlock - 1) / kBlock;
+  const int64_t ng = (nb + kGroup - 1) / kGroup;
+  const int64_t b = (int64_t)blockIdx.x * kGroup + t;
+  const float mu = scale2[ng];
+  const float c1 = b < nb ? dq_block_c1(W, n, b) : 0.0f;
+  const float cp = b < nb ? c1 - mu : 0.0f;                     // one fp32 rounding
+  // group max |c'| (bit order of non-negative floats)
+  uint32_t m = abs_bits(cp);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
+  if ((t & 63) == 0) s_red[t >> 6] = m;
+  __syncthreads();
+  m = max(max(s_red[0], s_red[1]), max(s_red[2], s_red[3]));
+  const double top = dq == 1 ? 127.0 : 448.0;
+  // correctly rounded fp32 quotient (fp64 quotient of fp32 values, rounded once more)
+  const float step = (float)((double)__uint_as_float(m) / top);
+  const double sd = (double)step, x = fabs((double)cp);
+  uint32_t code = 0;
+  if (step > 0.0f) {
+    if (dq == 1) {
+      // q = number of half-steps strictly below |c'|, at most 127 (exact in fp64)
+      int q = (int)floor(x / sd + 0.5);
+      q = q < 0 ? 0 : (q > 127 ? 127 : q);
+      while (q > 0 && !(x > (2.0 * q - 1.0) * sd * 0.5)) --q;
+      while (q < 127 && x > (2.0 * q + 1.0) * sd * 0.5) ++q;
+      code = (uint32_t)(uint8_t)(int8_t)(cp < 0.0f ? -q : q);
+    } else {
+      // k = number of E4M3 midpoints strictly below |c'|/step (binary search on
+      // exact thresholds), a tie going to the even code
+      int lo = 0, hi = 126;                                       // answer in [0, 126]
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        const double thr = 0.5 * (e4m3_mag(mid) + e4m3_mag(mid + 1)) * sd;
+        if (x > thr) lo = mid + 1; else hi = mid;
+      }
+      int k = lo;
+      if (k < 126 && x == 0.5 * (e4m3_mag(k) + e4m3_mag(k + 1)) * sd && ((k + 1) & 1) == 0) ++k;
+      code = (uint32_t)k | ((cp < 0.0f && k != 0) ? 0x80u : 0u);
+    }
+  }
+  if (b < nb) scale8[b] = (uint8_t)code;
+  if (t == 0) scale2[blockIdx.x] = step;
+}
+
+hipError_t launch_dq_variant(const float* W, int64_t n, uint8_t* scale8, float* scale2, int dq,
+                             double* psum, hipStream_t st) {
+  const int64_t nb = (n + kBlock - 1) / kBlock;
+  const int64_t ng = (nb + kGroup - 1) / kGroup;
+  if (ng == 0 || dq == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_dq_psum, dim3((unsigned)ng), dim3(256), 0, st, W, n, psum);
+  hipLaunchKernelGGL(k_dq_mean, dim3(1), dim3(64), 0, st, psum, ng, nb, scale2);
+  hipLaunchKernelGGL(k_dq_second, dim3((unsigned)ng), dim3(256), 0, st, W, n, scale8, scale2, dq);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ launchers
 hipError_t launch_quantize(const float* W, int64_t n, uint8_t* codes, uint8_t* scale8,
                            float* scale2, int32_t* flags, const Codebook& cb, hipStream_t st) {
@@ -253,17 +382,18 @@ hipError_t launch_quantize(const float* W, int64_t n, uint8_t* codes, uint8_t* s
 }
 
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scale8, const float* scale2,
-                          int64_t n, bool bf16, void* out, const Codebook& cb, hipStream_t st) {
+                          int64_t n, bool bf16, void* out, const Codebook& cb, hipStream_t st,
+                          int dq) {
   const int64_t n8 = (n + 7) / 8;
   if (n8 == 0) return hipSuccess;
   int64_t blocks = (n8 + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   if (bf16)
     hipLaunchKernelGGL(k_dequant<true>, dim3((unsigned)blocks), dim3(256), 0, st, codes, scale8,
-                       scale2, n, out, cb);
+                       scale2, n, out, cb, dq);
   else
     hipLaunchKernelGGL(k_dequant<false>, dim3((unsigned)blocks), dim3(256), 0, st, codes, scale8,
-                       scale2, n, out, cb);
+                       scale2, n, out, cb, dq);
   return hipGetLastError();
 }
 

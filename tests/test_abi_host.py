@@ -180,6 +180,28 @@ def test_adamw_validation(L):
     assert fp(A16, None, A16, A16, A16, 100, ctypes.byref(h), None, 1 << 20, None) == 4
 
 
+def test_dq_variant_sizes_and_validation(L):
+    for n in (0, 1, 16384, 16385, 4096 * 4096):
+        c, s8, s2 = nf4.sizes(n)
+        assert qb.qlora_quant_sizes_dq(n, "uint8") == (c, s8, s2, 0)
+        ng = s2 // 4
+        for v in ("int8_mean", "fp8_mean"):
+            got = qb.qlora_quant_sizes_dq(n, v)
+            assert got[:2] == (c, s8) and got[2] == s2 + (4 if n else 0)
+            assert got[3] >= 8 * ng and got[3] % 256 == 0
+    assert L.qlora_quant_sizes_dq(10, 3, None, None, None, None) == 1
+    v1 = _view(128 * 128)
+    v1.dq = 1
+    # the fused kernels and the plain quantizer reject a variant view
+    assert L.qlora_linear_fwd(A16, 8, 128, ctypes.byref(v1), 128, A16, A16, 8, 2.0, A16, None, A16,
+                              1 << 30, None) == 1
+    assert L.qlora_quantize_nf4_dq(A16, 128 * 128, ctypes.byref(v1), None, None) == 1
+    # the workspace quantizer needs its workspace
+    assert L.qlora_quantize_nf4_dq_ws(A16, 128 * 128, ctypes.byref(v1), None, None, 0, None) == 4
+    v1.dq = 7
+    assert L.qlora_dequant(ctypes.byref(v1), 0, A16, None) == 1
+
+
 def test_no_device_status(L):
     import torch
     if torch.cuda.is_available():
