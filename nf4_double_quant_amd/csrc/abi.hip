@@ -78,8 +78,8 @@ struct LaunchTimer {
   void clear() {
     for (auto& v : ev) {
       for (auto& p : v) {
-        hipEventDestroy(p.first);
-        hipEventDestroy(p.second);
+        (void)hipEventDestroy(p.first);    // diagnostics: nothing to do on failure
+        (void)hipEventDestroy(p.second);
       }
       v.clear();
     }
@@ -91,16 +91,20 @@ template <class F>
 hipError_t timed(int cls, hipStream_t st, F&& f) {
   if (!g_timer.on || !((g_timer.mask >> cls) & 1u)) return f();
   hipEvent_t a, b;
-  if (hipEventCreate(&a) != hipSuccess) return hipErrorUnknown;
-  if (hipEventCreate(&b) != hipSuccess) {
-    hipEventDestroy(a);
-    return hipErrorUnknown;
+  hipError_t e = hipEventCreate(&a);
+  if (e != hipSuccess) return e;
+  if ((e = hipEventCreate(&b)) != hipSuccess) {
+    (void)hipEventDestroy(a);
+    return e;
   }
-  hipEventRecord(a, st);
-  const hipError_t e = f();
-  hipEventRecord(b, st);
+  if ((e = hipEventRecord(a, st)) == hipSuccess && (e = f()) == hipSuccess) e = hipEventRecord(b, st);
+  if (e != hipSuccess) {
+    (void)hipEventDestroy(a);
+    (void)hipEventDestroy(b);
+    return e;
+  }
   g_timer.ev[cls].push_back({a, b});
-  return e;
+  return hipSuccess;
 }
 
 #define QL_TRY(expr)                                  \
