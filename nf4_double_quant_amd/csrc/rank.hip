@@ -6,9 +6,9 @@
 // bf16) and use v_mfma_f32_16x16x32_bf16 on fragments that never need a
 // transposed copy in memory:
 //  * k_rank_down: planes of P·Q over K-slices, P = X or dY ([M][K], K-major,
-//    loaded straight into A fragments), Q = A ([K][r]: staged in LDS and
-//    gathered with ds_read_b64_tr_b16) or Bᵀ (B is [r][K], K-major: direct
-//    16-byte loads).
+//    streamed into LDS by buffer_load ... lds and read as A fragments), Q = A
+//    ([K][r]: staged in LDS and gathered with ds_read_b64_tr_b16) or Bᵀ (B is
+//    [r][K], K-major: staged in LDS, read with ds_read_b128).
 //  * k_rank_grad: planes of Σ_m BIG[m][p]·SMALL[m][j] over token slices; both
 //    operands are token-major, staged in LDS as [m][·] rows and gathered
 //    with ds_read_b64_tr_b16 (4 consecutive tokens of one column per read).
@@ -56,60 +56,99 @@ constexpr int kDownRows = 128;    // rows of P per workgroup (4 waves × 32)
 constexpr int kDownK = 512;       // k-slice per workgroup
 constexpr int kDownLd = 80;       // LDS row stride (bf16) of the [k][j] Q tile: 64 + 16 pad
 constexpr int kDownKLd = kDownK + 8;   // LDS row stride (bf16) of the [j][k] Q tile
+constexpr int kWaveStage = 32 * 64;    // one wave's 32 rows × 64 k of P (4 KB)
+
+// s_waitcnt vmcnt(N) (N < 16), other counters not waited on
+template <int N>
+__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt((0xF << 8) | (0x7 << 4) | N); }
+
+// 16-byte chunk swizzle of a 128-byte P row
+__device__ __forceinline__ int pswz(int row) { return (row >> 1) & 7; }
+
 
 }  // namespace
 
 // part[z][m][j] = Σ_{k in slice z} P[m][k]·Q(k, j),  j in [64 c, 64 c + 64).
 // kQRowMajorK: Q(k, j) = Bsrc[j][k] (K-major rows of length K); otherwise
 // Q(k, j) = Asrc[k][j] (row length r).
+//
+// P streams memory -> LDS by buffer_load ... lds: each wave owns 32 rows and
+// moves them in 64-k stages (8 rows × 128 B per instruction, whole cache
+// lines) through a 4-slot ring of its own, so the only waits are the wave's
+// own vmcnt; 16-byte chunks are XOR-swizzled by (row / 2) % 8 so the A
+// fragments (16 rows × 16 B per read) hit every bank once.
 template <bool kQRowMajorK>
 __global__ __launch_bounds__(256) void k_rank_down(const uint16_t* __restrict__ P, int64_t M,
                                                    int64_t K, const uint16_t* __restrict__ Q,
                                                    int r, float* __restrict__ part) {
   __shared__ __attribute__((aligned(16))) uint16_t s_q[kQRowMajorK ? 64 * kDownKLd : kDownK * kDownLd];
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  // ring slots in separate arrays: the compiler can tell a slot being read
+  // from the slots the DMA is filling
+  __shared__ __attribute__((aligned(16))) uint16_t s_p0[4 * kWaveStage], s_p1[4 * kWaveStage],
+      s_p2[4 * kWaveStage], s_p3[4 * kWaveStage];
+  const int t = threadIdx.x, lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int64_t m0 = (int64_t)blockIdx.x * kDownRows;
   const int64_t k0 = (int64_t)blockIdx.y * kDownK;
   const int c0 = blockIdx.z * 64;
   const int64_t kn = min((int64_t)kDownK, K - k0);       // valid k in this slice (multiple of 8)
+  const int64_t mrows = min((int64_t)kDownRows, M - m0);
 
+  // ---- Q tile loads (registers), issued first
+  constexpr int kQLoads = kQRowMajorK ? 64 * kDownK / 8 / 256 : kDownK * 8 / 256;
+  uint4 vq[kQLoads];
   if (!kQRowMajorK) {
-    // stage Q[k0:k0+512][c0:c0+64]; rows past K and columns past r read 0.
-    // All 16 loads of a thread are in flight before the first store.
+    // Q[k0:k0+512][c0:c0+64]; rows past K and columns past r read 0
     const Rsrc rq = rsrc(Q + k0 * r, kn * r * 2);
-    uint4 v[kDownK * 8 / 256];
 #pragma unroll
-    for (int u = 0; u < kDownK * 8 / 256; ++u) {
+    for (int u = 0; u < kQLoads; ++u) {
       const int i = u * 256 + t, row = i >> 3, col = c0 + (i & 7) * 8;
-      v[u] = bload16(rq, col < r ? (uint32_t)((row * r + col) * 2) : kOob);
+      vq[u] = bload16(rq, col < r ? (uint32_t)((row * r + col) * 2) : kOob);
     }
-#pragma unroll
-    for (int u = 0; u < kDownK * 8 / 256; ++u) {
-      const int i = u * 256 + t;
-      *reinterpret_cast<uint4*>(s_q + (i >> 3) * kDownLd + (i & 7) * 8) = v[u];
-    }
-    __syncthreads();
   } else {
-    // stage Q[c0:c0+64][k0:k0+512] (rows j of B, K-major); rows past r and
-    // columns past K read 0.  Row stride 1040 bytes: the 16 rows one
-    // ds_read_b128 touches fall in different banks.
+    // Q[c0:c0+64][k0:k0+512] (rows j of B, K-major); rows past r and columns past K read 0
     const Rsrc rq = rsrc(Q + k0, ((int64_t)(r - 1) * K + kn) * 2);
-    uint4 v[64 * kDownK / 8 / 256];
 #pragma unroll
-    for (int u = 0; u < 64 * kDownK / 8 / 256; ++u) {
+    for (int u = 0; u < kQLoads; ++u) {
       const int i = u * 256 + t, row = i >> 6, ch = i & 63;     // 64 rows × 64 chunks
       const int j = c0 + row, kk = ch * 8;
-      v[u] = bload16(rq, (j < r && kk < kn) ? (uint32_t)(((int64_t)j * K + kk) * 2) : kOob);
+      vq[u] = bload16(rq, (j < r && kk < kn) ? (uint32_t)(((int64_t)j * K + kk) * 2) : kOob);
     }
-#pragma unroll
-    for (int u = 0; u < 64 * kDownK / 8 / 256; ++u) {
-      const int i = u * 256 + t;
-      *reinterpret_cast<uint4*>(s_q + (i >> 6) * kDownKLd + (i & 63) * 8) = v[u];
-    }
-    __syncthreads();
   }
-  const int64_t mrows = min((int64_t)kDownRows, M - m0);
+
+  // ---- P stages: stage st covers k0 + 64 st .. +63; chunks past kn or rows
+  // past M read 0 (a slice shorter than 512 streams zero stages)
   const Rsrc rp = rsrc(P + m0 * K + k0, mrows > 0 ? ((mrows - 1) * K + kn) * 2 : 0);
+  auto slot = [&](int st) -> uint16_t* {
+    uint16_t* s = (st & 3) == 0 ? s_p0 : (st & 3) == 1 ? s_p1 : (st & 3) == 2 ? s_p2 : s_p3;
+    return s + w * kWaveStage;
+  };
+  auto dma = [&](int st) {
+    uint16_t* dst = slot(st);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int row = w * 32 + q * 8 + (lane >> 3);
+      const int kk = st * 64 + (((lane & 7) ^ pswz(row)) << 3);
+      const uint32_t off = (row < mrows && kk < kn) ? (uint32_t)((row * K + kk) * 2) : kOob;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rp, (__attribute__((address_space(3))) void*)(dst + q * 8 * 64), 16, off, 0, 0, 0);
+    }
+  };
+#pragma unroll
+  for (int st = 0; st < 4; ++st) dma(st);
+
+  // ---- Q tile to LDS once its loads are in (the P stages stay in flight)
+#pragma unroll
+  for (int u = 0; u < kQLoads; ++u) {
+    const int i = u * 256 + t;
+    if (!kQRowMajorK)
+      *reinterpret_cast<uint4*>(s_q + (i >> 3) * kDownLd + (i & 7) * 8) = vq[u];
+    else   // row stride 1040 bytes: the 16 rows one ds_read_b128 touches fall in different banks
+      *reinterpret_cast<uint4*>(s_q + (i >> 6) * kDownKLd + (i & 63) * 8) = vq[u];
+  }
+  // LDS-only barrier: the P stages stay in flight (a fence here would wait
+  // for them, since they write LDS)
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
   f32x4 acc[2][4];
 #pragma unroll
@@ -118,32 +157,34 @@ __global__ __launch_bounds__(256) void k_rank_down(const uint16_t* __restrict__ 
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
   const int g = lane >> 4, l16 = lane & 15;
-  // P fragments for 32-wide step kq are loaded kPre steps ahead, so memory
-  // latency overlaps the MFMAs.
-  constexpr int kSteps = kDownK / 32, kPre = 3;
-  bf16x8 a[kSteps][2];
-  auto load = [&](int kq) {
-    const int kk = kq * 32 + 8 * g;                // this lane's 8 k, relative to k0
+  const int sw = pswz(l16);              // = pswz of rows w*32 + 16 i + l16
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int row = w * 32 + i * 16 + l16;
-      const uint32_t off = kk < kn ? (uint32_t)((row * K + kk) * 2) : kOob;
-      a[kq][i] = __builtin_bit_cast(bf16x8, bload16(rp, off));
-    }
-  };
+  for (int st = 0; st < kDownK / 64; ++st) {
+    // this wave's DMA for stage st is in once at most the later stages' are outstanding
+    const int later = min(3, kDownK / 64 - 1 - st);
+    if (later == 3) wait_vm<12>(); else if (later == 2) wait_vm<8>(); else if (later == 1) wait_vm<4>(); else wait_vm<0>();
+    const uint16_t* sp = slot(st);
 #pragma unroll
-  for (int kq = 0; kq < kPre; ++kq) load(kq);
-#pragma unroll
-  for (int kq = 0; kq < kSteps; ++kq) {
-    if (kq + kPre < kSteps) load(kq + kPre);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const bf16x8 b =
-          kQRowMajorK ? *reinterpret_cast<const bf16x8*>(s_q + (j * 16 + l16) * kDownKLd + kq * 32 + 8 * g)
-                      : frag_tr(s_q, kDownLd, kq * 32, j * 16, lane);
+    for (int h = 0; h < 2; ++h) {
+      const int kq = st * 2 + h;
+      bf16x8 a[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[kq][i], b, acc[i][j], 0, 0, 0);
+        a[i] = *reinterpret_cast<const bf16x8*>(sp + (i * 16 + l16) * 64 + (((4 * h + g) ^ sw) << 3));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bf16x8 b =
+            kQRowMajorK ? *reinterpret_cast<const bf16x8*>(s_q + (j * 16 + l16) * kDownKLd + kq * 32 + 8 * g)
+                        : frag_tr(s_q, kDownLd, kq * 32, j * 16, lane);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b, acc[i][j], 0, 0, 0);
+      }
+    }
+    // the slot is free again once this stage's fragments are in registers
+    if (st + 4 < kDownK / 64) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+      dma(st + 4);
     }
   }
   // lane holds rows 4*(lane/16)+v of column lane%16 in each 16×16 block
