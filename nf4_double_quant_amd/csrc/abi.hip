@@ -304,8 +304,9 @@ int qlora_linear_fwd(const qlora_bf16* X, int64_t M, int64_t d, const qlora_nf4d
     // T = X·A as split-K planes, summed into T_out (fp32) and s·T (bf16)
     QL_RUN(QLORA_K_ADAPTER, hs, launch_rank_down(false, X, M, d, A, (int)r, Tpart, hs));
     QL_RUN(QLORA_K_ADAPTER, hs,
-           launch_reduce_planes(Tpart, (int)L.t_splits, M * r, M * r, T_out, lora ? sT : nullptr,
-                                s, hs));
+           launch_reduce_planes(ReduceJob{Tpart, (int)L.t_splits, M * r, M * r, T_out,
+                                          lora ? sT : nullptr, s},
+                                ReduceJob{}, hs));
   }
   QL_RUN(QLORA_K_MAIN_GEMM, hs,
          launch_qgemm(false, X, d, W->codes, W->scale8, W->scale2, d, sT, r, B, o, M, o, d,
@@ -428,27 +429,27 @@ int qlora_linear_bwd(const qlora_bf16* dY, const qlora_bf16* X, const float* T, 
   const bool lora = r > 0 && s != 0.0f;
 
   if (r > 0) {
-    // T when the caller did not keep it: s·T in bf16 from the planes.  A
-    // given T enters dB's kernel as fp32, scaled and rounded to bf16 there.
-    if (T == nullptr) {
+    // U = dY·Bᵀ as split planes (B [r][o] is the K-major operand); T as
+    // planes too when the caller did not keep it
+    if (T == nullptr)
       QL_RUN(QLORA_K_ADAPTER, hs, launch_rank_down(false, X, M, d, A, (int)r, Tpart, hs));
-      QL_RUN(QLORA_K_ADAPTER, hs,
-             launch_reduce_planes(Tpart, (int)L.t_splits, M * r, M * r, nullptr, sT, s, hs));
-    }
-    // s·U = s·dY·Bᵀ (B [r][o] is the K-major operand)
     QL_RUN(QLORA_K_ADAPTER, hs, launch_rank_down(true, dY, M, o, B, (int)r, Upart, hs));
+    // s·U and s·T in bf16 (a given T is one plane)
     QL_RUN(QLORA_K_ADAPTER, hs,
-           launch_reduce_planes(Upart, (int)L.u_splits, M * r, M * r, nullptr, sU, s, hs));
-    // dA = Xᵀ·(s·U) [d][r] and dB = (s·T)ᵀ·dY [r][o], reductions over the tokens
-    QL_RUN(QLORA_K_GRADS, hs, launch_rank_grad(true, X, d, sU, false, 1.0f, (int)r, M, dApart, hs));
-    if (T != nullptr)
-      QL_RUN(QLORA_K_GRADS, hs, launch_rank_grad(false, dY, o, T, true, s, (int)r, M, dBpart, hs));
-    else
-      QL_RUN(QLORA_K_GRADS, hs, launch_rank_grad(false, dY, o, sT, false, 1.0f, (int)r, M, dBpart, hs));
+           launch_reduce_planes(
+               ReduceJob{Upart, (int)L.u_splits, M * r, M * r, nullptr, sU, s},
+               T != nullptr ? ReduceJob{T, 1, M * r, M * r, nullptr, sT, s}
+                            : ReduceJob{Tpart, (int)L.t_splits, M * r, M * r, nullptr, sT, s},
+               hs));
+    // dA = Xᵀ·(s·U) [d][r] and dB = (s·T)ᵀ·dY [r][o], reductions over the
+    // tokens, in one launch; then both sums in one launch
     QL_RUN(QLORA_K_GRADS, hs,
-           launch_reduce_planes(dApart, (int)L.g_splits, d * r, d * r, nullptr, dA, 1.0f, hs));
+           launch_rank_grads(RankGradJob{X, d, sU, dApart, true, 0},
+                             RankGradJob{dY, o, sT, dBpart, false, 0}, (int)r, M, hs));
     QL_RUN(QLORA_K_GRADS, hs,
-           launch_reduce_planes(dBpart, (int)L.g_splits, r * o, r * o, nullptr, dB, 1.0f, hs));
+           launch_reduce_planes(ReduceJob{dApart, (int)L.g_splits, d * r, d * r, nullptr, dA, 1.0f},
+                                ReduceJob{dBpart, (int)L.g_splits, r * o, r * o, nullptr, dB, 1.0f},
+                                hs));
   }
   if (dX != nullptr) {
     QL_RUN(QLORA_K_MAIN_GEMM, hs,

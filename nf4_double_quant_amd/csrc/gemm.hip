@@ -4,16 +4,18 @@
 
 namespace qlora {
 
-// Sum of split-K planes over a contiguous [rows][cols] region:
-// out_f32 = Σ_z part[z]; out_bf16 = bf16(scale·Σ_z part[z]).  Four
-// elements per thread, fixed summation order.
-__global__ __launch_bounds__(256) void k_reduce_planes(const float* __restrict__ part, int splits,
-                                                       int64_t plane, int64_t count,
-                                                       float* __restrict__ out_f32,
-                                                       uint16_t* __restrict__ out_bf16, float scale) {
-  const int64_t n4 = count / 4;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4;
-       i += (int64_t)gridDim.x * blockDim.x) {
+// Sum of split planes over a contiguous region: out_f32 = Σ_z part[z];
+// out_bf16 = bf16(scale·Σ_z part[z]).  Four elements per thread, fixed
+// summation order.  Workgroups [0, blocks_a) serve job a, the rest job b.
+__global__ __launch_bounds__(256) void k_reduce_planes(ReduceJob a, ReduceJob b, int blocks_a) {
+  const bool first = (int)blockIdx.x < blocks_a;
+  const ReduceJob& jo = first ? a : b;
+  const int64_t blk = first ? blockIdx.x : blockIdx.x - blocks_a;
+  const int64_t nblk = first ? blocks_a : gridDim.x - blocks_a;
+  const float* part = jo.part;
+  const int splits = jo.splits;
+  const int64_t plane = jo.plane, n4 = jo.count / 4;
+  for (int64_t i = blk * blockDim.x + threadIdx.x; i < n4; i += nblk * blockDim.x) {
     // planes summed in order, four loads in flight at a time
     float4 s = reinterpret_cast<const float4*>(part)[i];
     int z = 1;
@@ -28,12 +30,12 @@ __global__ __launch_bounds__(256) void k_reduce_planes(const float* __restrict__
       const float4 v = reinterpret_cast<const float4*>(part + (int64_t)z * plane)[i];
       s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
     }
-    if (out_f32) reinterpret_cast<float4*>(out_f32)[i] = s;
-    if (out_bf16) {
+    if (jo.out_f32) reinterpret_cast<float4*>(jo.out_f32)[i] = s;
+    if (jo.out_bf16) {
       uint2 o;
-      o.x = pack_bf16x2(scale * s.x, scale * s.y);
-      o.y = pack_bf16x2(scale * s.z, scale * s.w);
-      reinterpret_cast<uint2*>(out_bf16)[i] = o;
+      o.x = pack_bf16x2(jo.scale * s.x, jo.scale * s.y);
+      o.y = pack_bf16x2(jo.scale * s.z, jo.scale * s.w);
+      reinterpret_cast<uint2*>(jo.out_bf16)[i] = o;
     }
   }
 }
@@ -44,15 +46,15 @@ __global__ __launch_bounds__(256) void k_fill_zero_bf16(uint16_t* __restrict__ y
     y[i] = 0;
 }
 
-// fp32 -> bf16(scale·x), elementwise.
 // ------------------------------------------------------------------ launchers
-hipError_t launch_reduce_planes(const float* part, int splits, int64_t plane, int64_t count,
-                                float* out_f32, uint16_t* out_bf16, float scale, hipStream_t st) {
-  if (count == 0) return hipSuccess;
-  int64_t blocks = (count / 4 + 255) / 256;
-  if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(k_reduce_planes, dim3((unsigned)blocks), dim3(256), 0, st, part, splits,
-                     plane, count, out_f32, out_bf16, scale);
+hipError_t launch_reduce_planes(const ReduceJob& a, const ReduceJob& b, hipStream_t st) {
+  auto blocks = [](int64_t count) -> int {
+    const int64_t n = (count / 4 + 255) / 256;
+    return (int)(n > 4096 ? 4096 : n);
+  };
+  const int ba = blocks(a.count), bb = blocks(b.count);
+  if (ba + bb == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_reduce_planes, dim3((unsigned)(ba + bb)), dim3(256), 0, st, a, b, ba);
   return hipGetLastError();
 }
 

@@ -36,18 +36,34 @@ hipError_t launch_qgemm(bool trans_w, const uint16_t* A, int64_t lda, const uint
 int rank_down_splits(int64_t K);
 hipError_t launch_rank_down(bool q_rowmajor_k, const uint16_t* P, int64_t M, int64_t K,
                             const uint16_t* Q, int r, float* part, hipStream_t st);
-// part[z] = Σ_{m in token slice z} big[m][p]·small[m][j], stored [P][r] when
-// out_pj, else [r][P]; rank_grad_splits(M) planes.  small is bf16, or fp32
-// entering as bf16(small_scale · small) when small_f32.
+// One product of launch_rank_grads: part[z] = Σ_{m in token slice z}
+// big[m][p]·small[m][j] (big [M][P], small [M][r], both bf16), stored
+// [P][r] when out_pj, else [r][P]; rank_grad_splits(M) planes.  A job with
+// P == 0 is skipped.
+struct RankGradJob {
+  const uint16_t* big;
+  int64_t P;
+  const uint16_t* small;
+  float* part;
+  bool out_pj;
+  int tiles;   // set by the launcher
+};
 int rank_grad_splits(int64_t M);
-hipError_t launch_rank_grad(bool out_pj, const uint16_t* big, int64_t P, const void* small,
-                            bool small_f32, float small_scale, int r, int64_t M, float* part,
-                            hipStream_t st);
+hipError_t launch_rank_grads(RankGradJob a, RankGradJob b, int r, int64_t M, hipStream_t st);
 
 // Contiguous split planes [splits][count] (count % 4 == 0) -> their sum, in
-// plane order: out_f32 = Σ, out_bf16 = bf16(scale·Σ).
-hipError_t launch_reduce_planes(const float* part, int splits, int64_t plane, int64_t count,
-                                float* out_f32, uint16_t* out_bf16, float scale, hipStream_t st);
+// plane order: out_f32 = Σ, out_bf16 = bf16(scale·Σ).  With one plane it is
+// the conversion to bf16(scale·x).  Two independent jobs per launch (the
+// second may have count 0).
+struct ReduceJob {
+  const float* part;
+  int splits;
+  int64_t plane, count;
+  float* out_f32;
+  uint16_t* out_bf16;
+  float scale;
+};
+hipError_t launch_reduce_planes(const ReduceJob& a, const ReduceJob& b, hipStream_t st);
 hipError_t launch_fill_zero_bf16(uint16_t* y, int64_t n, hipStream_t st);
 
 // Few-token forward (M <= kGemvMaxTokens): Tpart [gemv_tsplits(d)][M][r]

@@ -9,13 +9,16 @@
 //    streamed into LDS by buffer_load ... lds and read as A fragments), Q = A
 //    ([K][r]: staged in LDS and gathered with ds_read_b64_tr_b16) or Bᵀ (B is
 //    [r][K], K-major: staged in LDS, read with ds_read_b128).
-//  * k_rank_grad: planes of Σ_m BIG[m][p]·SMALL[m][j] over token slices; both
-//    operands are token-major, staged in LDS as [m][·] rows and gathered
-//    with ds_read_b64_tr_b16 (4 consecutive tokens of one column per read).
+//  * k_rank_grad: planes of Σ_m BIG[m][p]·SMALL[m][j] over token slices, for
+//    dA and dB in one launch; both operands are token-major, streamed into
+//    LDS as [m][·] rows and gathered with ds_read_b64_tr_b16 (4 consecutive
+//    tokens of one column per read).
 // Split planes are summed in a fixed order by k_reduce_planes, so results
 // are bitwise reproducible.  (Summing them inside these kernels, with the
 // last workgroup of a tile reducing, costs more on this chip: every
 // device-scope release fence writes back the XCD's whole L2.)
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace qlora {
@@ -204,93 +207,161 @@ __global__ __launch_bounds__(256) void k_rank_down(const uint16_t* __restrict__ 
 namespace {
 constexpr int kGradP = 128;       // big-dimension columns per workgroup (4 waves × 32)
 constexpr int kGradM = 512;       // tokens per workgroup (split of the reduction)
-constexpr int kGradChunk = 64;    // tokens staged per LDS round
-constexpr int kBigLd = kGradP + 16;
-constexpr int kSmallLd = 64 + 16;
+constexpr int kGradChunk = 64;    // tokens per LDS stage
+constexpr int kBigStage = kGradChunk * kGradP;   // bf16 elements of a BIG stage (16 KB)
+constexpr int kSmallStage = kGradChunk * 64;     // bf16 elements of a SMALL stage (8 KB)
+
+// 16-byte chunk swizzles of the token-major stages.  Even XOR values keep
+// each 32-byte pair together; a half-wave of a transposed fragment read
+// touches rows R..R+3 and R+8..R+11 (R % 4 == 0), 32 bytes each, and these
+// put the eight pieces in eight different 32-byte bank groups.
+__device__ __forceinline__ int big_swz(int row) {     // 256-byte rows
+  return 2 * ((row & 3) | (((row >> 3) & 1) << 2));
+}
+__device__ __forceinline__ int small_swz(int row) {   // 128-byte rows
+  return 2 * (((row >> 1) & 1) | (((row >> 3) & 1) << 1));
+}
+
+// LDS byte address of a pointer into a __shared__ array
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Byte offset, within a swizzled token-major stage, of the first of the two
+// ds_read_b64_tr_b16 of a 16x16x32 fragment: column x0 + lane%16, tokens
+// 8*(lane/16) .. +7 (the second read is 4 rows further; rows r, r+4 and
+// r+32 share a swizzle).
+template <bool kBig>
+__device__ __forceinline__ uint32_t frag_off(int x0, int lane) {
+  const int g = lane >> 4, s = lane & 15;
+  const int row = 8 * g + (s >> 2), col = x0 + 4 * (s & 3);
+  const int sw = kBig ? big_swz(row) : small_swz(row);
+  return (uint32_t)(row * (kBig ? 2 * kGradP : 128) + ((((col >> 3) ^ sw)) << 4) + (col & 7) * 2);
+}
+
+// The twelve transposed reads of one 32-token step: BIG fragments at b0, b1
+// (second read +1024 bytes), SMALL fragments at s0..s3 (+512 bytes).  The
+// reads target LDS filled by buffer_load ... lds, so they are issued here
+// with an explicit wait: the block returns with every result in place.
+struct GradFrags {
+  s16x4 b[2][2], s[4][2];
+};
+__device__ __forceinline__ void grad_reads(GradFrags& f, uint32_t b0, uint32_t b1, uint32_t s0,
+                                           uint32_t s1, uint32_t s2, uint32_t s3) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %12\n\t"
+      "ds_read_b64_tr_b16 %1, %12 offset:1024\n\t"
+      "ds_read_b64_tr_b16 %2, %13\n\t"
+      "ds_read_b64_tr_b16 %3, %13 offset:1024\n\t"
+      "ds_read_b64_tr_b16 %4, %14\n\t"
+      "ds_read_b64_tr_b16 %5, %14 offset:512\n\t"
+      "ds_read_b64_tr_b16 %6, %15\n\t"
+      "ds_read_b64_tr_b16 %7, %15 offset:512\n\t"
+      "ds_read_b64_tr_b16 %8, %16\n\t"
+      "ds_read_b64_tr_b16 %9, %16 offset:512\n\t"
+      "ds_read_b64_tr_b16 %10, %17\n\t"
+      "ds_read_b64_tr_b16 %11, %17 offset:512\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(f.b[0][0]), "=&v"(f.b[0][1]), "=&v"(f.b[1][0]), "=&v"(f.b[1][1]), "=&v"(f.s[0][0]),
+        "=&v"(f.s[0][1]), "=&v"(f.s[1][0]), "=&v"(f.s[1][1]), "=&v"(f.s[2][0]), "=&v"(f.s[2][1]),
+        "=&v"(f.s[3][0]), "=&v"(f.s[3][1])
+      : "v"(b0), "v"(b1), "v"(s0), "v"(s1), "v"(s2), "v"(s3)
+      : "memory");
+}
+__device__ __forceinline__ bf16x8 join(const s16x4 (&x)[2]) {
+  const s16x8 v = {x[0][0], x[0][1], x[0][2], x[0][3], x[1][0], x[1][1], x[1][2], x[1][3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
 }  // namespace
 
 // part[z][...] = Σ_{m in slice z} BIG[m][p]·SMALL[m][j] for p in a 128-wide
-// tile and j in [64 c, 64 c + 64).  kOutPJ: stored as [p][j] (row length r),
-// else as [j][p] (row length P).
-// kSmallF32: SMALL is fp32 and enters as bf16(small_scale · SMALL).
-template <bool kOutPJ, bool kSmallF32>
-__global__ __launch_bounds__(256) void k_rank_grad(const uint16_t* __restrict__ big, int64_t P,
-                                                   const void* __restrict__ small, float small_scale,
-                                                   int r, int64_t M, float* __restrict__ part) {
-  __shared__ __attribute__((aligned(16))) uint16_t s_big[kGradChunk * kBigLd];
-  __shared__ __attribute__((aligned(16))) uint16_t s_small[kGradChunk * kSmallLd];
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const int64_t p0 = (int64_t)blockIdx.x * kGradP;
+// tile and j in [64 c, 64 c + 64), for two independent products in one
+// launch (workgroups [0, a.tiles) take a, the rest b).  out_pj: stored as
+// [p][j] (row length r), else as [j][p] (row length P).
+//
+// BIG [64 tokens][128 p] and SMALL [64 tokens][64 j] stages stream memory ->
+// LDS by buffer_load ... lds (whole cache lines, 1 KB per instruction)
+// through a 3-slot ring, two stages ahead; one LDS barrier per stage.
+__global__ __launch_bounds__(256) void k_rank_grad(RankGradJob ja, RankGradJob jb, int r, int64_t M) {
+  __shared__ __attribute__((aligned(16))) uint16_t sb0[kBigStage], sb1[kBigStage], sb2[kBigStage];
+  __shared__ __attribute__((aligned(16))) uint16_t ss0[kSmallStage], ss1[kSmallStage], ss2[kSmallStage];
+  const int t = threadIdx.x, lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const bool first = (int)blockIdx.x < ja.tiles;
+  const uint16_t* big = first ? ja.big : jb.big;
+  const uint16_t* small = first ? ja.small : jb.small;
+  float* part = first ? ja.part : jb.part;
+  const int64_t P = first ? ja.P : jb.P;
+  const bool out_pj = first ? ja.out_pj : jb.out_pj;
+  const int64_t p0 = (int64_t)(first ? blockIdx.x : blockIdx.x - ja.tiles) * kGradP;
   const int64_t mz = (int64_t)blockIdx.y * kGradM;
   const int c0 = blockIdx.z * 64;
   const int64_t mlen = min((int64_t)kGradM, M - mz);
   const Rsrc rb = rsrc(big + mz * P, mlen * P * 2);
-  const Rsrc rs = rsrc(static_cast<const char*>(small) + mz * r * (kSmallF32 ? 4 : 2),
-                      mlen * r * (kSmallF32 ? 4 : 2));
+  const Rsrc rs = rsrc(small + mz * r, mlen * r * 2);
 
+  auto big_slot = [&](int c) -> uint16_t* { return c % 3 == 0 ? sb0 : c % 3 == 1 ? sb1 : sb2; };
+  auto small_slot = [&](int c) -> uint16_t* { return c % 3 == 0 ? ss0 : c % 3 == 1 ? ss1 : ss2; };
+  // stage c of the slice (tokens mz + 64 c ..); tokens past M, columns past
+  // P or r read 0.  Wave w moves BIG rows 16w .. 16w+15 and SMALL rows
+  // 16w .. 16w+15.
+  auto dma = [&](int c) {
+    uint16_t* sb = big_slot(c);
+    uint16_t* ss = small_slot(c);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {              // 4 rows × 256 bytes per instruction
+      const int q = 4 * w + u, row = 4 * q + (lane >> 4);
+      const int tok = c * kGradChunk + row;
+      const int64_t col = p0 + 8 * ((lane & 15) ^ big_swz(row));
+      const uint32_t off = (tok < mlen && col < P) ? (uint32_t)((tok * P + col) * 2) : kOob;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rb, (__attribute__((address_space(3))) void*)(sb + q * 512), 16, off, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {              // 8 rows × 128 bytes per instruction
+      const int q = 2 * w + u, row = 8 * q + (lane >> 3);
+      const int tok = c * kGradChunk + row;
+      const int col = c0 + 8 * ((lane & 7) ^ small_swz(row));
+      const uint32_t off = (tok < mlen && col < r) ? (uint32_t)((tok * r + col) * 2) : kOob;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)(ss + q * 512), 16, off, 0, 0, 0);
+    }
+  };
+
+  // the main loop and the epilogue, for one output layout (uniform per workgroup)
+  auto body = [&](auto pj_tag) {
+  constexpr bool kOutPJ = decltype(pj_tag)::value;
   f32x4 acc[2][4];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // BIG[mc:mc+64][p0:p0+128] and SMALL[mc:mc+64][c0:c0+64] of chunk c go
-  // through registers into LDS; the loads of chunk c+1 are issued before the
-  // MFMAs of chunk c, so memory latency overlaps them.
-  constexpr int kChunks = kGradM / kGradChunk;
-  constexpr int kSmallLoads = kSmallF32 ? 4 : 2;   // 16-byte loads per thread per chunk
-  uint4 vb[kChunks][4], vs[kChunks][kSmallLoads];
-  auto load = [&](int c) {
-    const int mc = c * kGradChunk;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int i = q * 256 + t;                 // 64 rows × 16 chunks
-      const int row = i >> 4, ch = i & 15;
-      const int64_t col = p0 + ch * 8;
-      vb[c][q] = bload16(rb, col < P ? (uint32_t)(((mc + row) * P + col) * 2) : kOob);
-    }
-#pragma unroll
-    for (int q = 0; q < kSmallLoads; ++q) {
-      const int i = q * 256 + t;
-      if (kSmallF32) {                           // 64 rows × 16 chunks of 4 fp32
-        const int row = i >> 4, col = c0 + (i & 15) * 4;
-        vs[c][q] = bload16(rs, col < r ? (uint32_t)(((mc + row) * r + col) * 4) : kOob);
-      } else {                                   // 64 rows × 8 chunks of 8 bf16
-        const int row = i >> 3, col = c0 + (i & 7) * 8;
-        vs[c][q] = bload16(rs, col < r ? (uint32_t)(((mc + row) * r + col) * 2) : kOob);
-      }
-    }
-  };
-  load(0);
+  constexpr int kChunks = kGradM / kGradChunk;   // a slice shorter than 512 streams zero stages
+  const uint32_t ob0 = frag_off<true>(w * 32, lane), ob1 = frag_off<true>(w * 32 + 16, lane);
+  const uint32_t os0 = frag_off<false>(0, lane), os1 = frag_off<false>(16, lane);
+  const uint32_t os2 = frag_off<false>(32, lane), os3 = frag_off<false>(48, lane);
+  dma(0);
+  dma(1);
 #pragma unroll
   for (int c = 0; c < kChunks; ++c) {
-    if (c + 1 < kChunks) load(c + 1);
-    __syncthreads();   // previous round's fragments are consumed
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int i = q * 256 + t;
-      *reinterpret_cast<uint4*>(s_big + (i >> 4) * kBigLd + (i & 15) * 8) = vb[c][q];
-    }
-#pragma unroll
-    for (int q = 0; q < kSmallLoads; ++q) {
-      const int i = q * 256 + t;
-      if (kSmallF32) {
-        const float4 x = __builtin_bit_cast(float4, vs[c][q]);
-        const uint2 b = make_uint2(pack_bf16x2(small_scale * x.x, small_scale * x.y),
-                                   pack_bf16x2(small_scale * x.z, small_scale * x.w));
-        *reinterpret_cast<uint2*>(s_small + (i >> 4) * kSmallLd + (i & 15) * 4) = b;
-      } else {
-        *reinterpret_cast<uint4*>(s_small + (i >> 3) * kSmallLd + (i & 7) * 8) = vs[c][q];
-      }
-    }
-    __syncthreads();
+    // this wave's part of stage c is in once at most stage c+1 is outstanding
+    if (c + 1 < kChunks) wait_vm<6>(); else wait_vm<0>();
+    // every wave's part has landed and every wave is done with stage c-1
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (c + 2 < kChunks) dma(c + 2);           // into the slot of stage c-1
+    const uint32_t ab = lds_addr(big_slot(c)), as = lds_addr(small_slot(c));
 #pragma unroll
     for (int kq = 0; kq < kGradChunk / 32; ++kq) {
+      // 32 tokens further: 32 rows of 256 (BIG) or 128 (SMALL) bytes
+      GradFrags f;
+      grad_reads(f, ab + ob0 + kq * 8192, ab + ob1 + kq * 8192, as + os0 + kq * 4096,
+                 as + os1 + kq * 4096, as + os2 + kq * 4096, as + os3 + kq * 4096);
       bf16x8 fb[2], fs[4];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) fb[i] = frag_tr(s_big, kBigLd, kq * 32, w * 32 + i * 16, lane);
+      for (int i = 0; i < 2; ++i) fb[i] = join(f.b[i]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) fs[j] = frag_tr(s_small, kSmallLd, kq * 32, j * 16, lane);
+      for (int j = 0; j < 4; ++j) fs[j] = join(f.s[j]);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -299,7 +370,7 @@ __global__ __launch_bounds__(256) void k_rank_grad(const uint16_t* __restrict__ 
                              : __builtin_amdgcn_mfma_f32_16x16x32_bf16(fs[j], fb[i], acc[i][j], 0, 0, 0);
     }
   }
-  // kOutPJ: block (i, j) is D[p][j]: lane holds j = lane%16, p rows 4*(lane/16)+v.
+  // out_pj: block (i, j) is D[p][j]: lane holds j = lane%16, p rows 4*(lane/16)+v.
   // else:   block (i, j) is D[j][p]: lane holds p = lane%16, j rows 4*(lane/16)+v.
   const int g = lane >> 4, l16 = lane & 15;
   float* out = part + (int64_t)blockIdx.y * P * r;
@@ -319,6 +390,8 @@ __global__ __launch_bounds__(256) void k_rank_grad(const uint16_t* __restrict__ 
           if (p < P && jj < r) out[(int64_t)jj * P + p] = acc[i][j][v];
         }
       }
+  };
+  if (out_pj) body(std::true_type{}); else body(std::false_type{});
 }
 
 int rank_down_splits(int64_t K) { return (int)((K + kDownK - 1) / kDownK); }
@@ -336,20 +409,12 @@ hipError_t launch_rank_down(bool q_rowmajor_k, const uint16_t* P, int64_t M, int
   return hipGetLastError();
 }
 
-hipError_t launch_rank_grad(bool out_pj, const uint16_t* big, int64_t P, const void* small,
-                            bool small_f32, float small_scale, int r, int64_t M, float* part,
-                            hipStream_t st) {
-  if (P == 0 || r == 0) return hipSuccess;
-  dim3 grid((unsigned)((P + kGradP - 1) / kGradP), (unsigned)rank_grad_splits(M),
-            (unsigned)((r + 63) / 64));
-#define QL_GRAD(PJ, F32) \
-  hipLaunchKernelGGL((k_rank_grad<PJ, F32>), grid, dim3(256), 0, st, big, P, small, small_scale, r, M, part)
-  if (out_pj) {
-    if (small_f32) QL_GRAD(true, true); else QL_GRAD(true, false);
-  } else {
-    if (small_f32) QL_GRAD(false, true); else QL_GRAD(false, false);
-  }
-#undef QL_GRAD
+hipError_t launch_rank_grads(RankGradJob a, RankGradJob b, int r, int64_t M, hipStream_t st) {
+  a.tiles = a.P > 0 ? (int)((a.P + kGradP - 1) / kGradP) : 0;
+  b.tiles = b.P > 0 ? (int)((b.P + kGradP - 1) / kGradP) : 0;
+  if (a.tiles + b.tiles == 0 || r == 0 || M == 0) return hipSuccess;
+  dim3 grid((unsigned)(a.tiles + b.tiles), (unsigned)rank_grad_splits(M), (unsigned)((r + 63) / 64));
+  hipLaunchKernelGGL(k_rank_grad, grid, dim3(256), 0, st, a, b, r, M);
   return hipGetLastError();
 }
 
