@@ -92,6 +92,8 @@ def test_tiny_128_workload():
     (520, 640, 776, 64, 2.0),     # 3×4 tiles of 256, ragged
     (64, 256, 512, 128, 0.25),    # rank above one k-step
     (33, 320, 136, 24, 1.5),      # rank not a multiple of 16
+    (1100, 128, 200, 256, 0.5),   # largest rank (4 column blocks), 3 token slices, ragged
+    (700, 64, 520, 72, 1.0),      # rank just past one column block; K-slice of U ragged
 ])
 def test_ragged_shapes(M, d, o, r, s):
     full_parity(M, d, o, r, s, seed=M * 7 + d)
