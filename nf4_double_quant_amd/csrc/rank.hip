@@ -61,9 +61,13 @@ constexpr int kDownLd = 80;       // LDS row stride (bf16) of the [k][j] Q tile:
 constexpr int kDownKLd = kDownK + 8;   // LDS row stride (bf16) of the [j][k] Q tile
 constexpr int kWaveStage = 32 * 64;    // one wave's 32 rows × 64 k of P (4 KB)
 
-// s_waitcnt vmcnt(N) (N < 16), other counters not waited on
+// s_waitcnt vmcnt(N) (N < 64: low 4 bits in [3:0], high 2 in [15:14]),
+// other counters not waited on
 template <int N>
-__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt((0xF << 8) | (0x7 << 4) | N); }
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt(((N >> 4) << 14) | (0xF << 8) | (0x7 << 4) | (N & 0xF));
+}
 
 // 16-byte chunk swizzle of a 128-byte P row
 __device__ __forceinline__ int pswz(int row) { return (row >> 1) & 7; }
