@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--decode-sets", type=int, default=16,
                     help="independent weight sets cycled by the decode measurement")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-blocks", action="store_true",
+                    help="skip the 7B / 65B-style block measurements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--pmc", action="store_true",
@@ -244,6 +246,7 @@ def main():
                  for name, (ms, n) in per_class.items() if n}
 
     decode = None if args.no_decode else bench_decode(args, qb, torch, np, synth, dev)
+    blocks = None if args.no_blocks else bench_blocks(qb, torch, synth, dev)
     formats = format_errors(qb, torch, W)
     merge_res = merge_study(qb, torch, W, q, X, A, B, s)
     optim = optimizer_study(qb, torch, synth, dev)
@@ -262,7 +265,8 @@ def main():
                    "step": "quantize NF4+DQ + fwd + bwd (dX, dA, dB)", "flop_per_step": flops,
                    "parallelism": "single GPU"},
         "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
-        "roofline": roofline, "breakdown": breakdown, "decode": decode, "formats": formats,
+        "roofline": roofline, "breakdown": breakdown, "decode": decode, "blocks": blocks,
+        "formats": formats,
         "merge": merge_res, "optimizer": optim,
         "cpu_baseline": cpu,
     }
@@ -394,6 +398,88 @@ def bench_decode(args, qb, torch, np, synth, dev):
     return {"workload": "decode_mlp_7b: gate/up 4096->11008, down 11008->4096, r=16, fwd only; "
                         "M16_16_adapters: one adapter per token (16 adapters per projection)",
             "weight_sets_cycled": len(sets), "peak_GBps": PEAK_HBM_GBPS, **res}
+
+
+def bench_blocks(qb, torch, synth, dev, steps=5, warmup=2):
+    """Forward + backward over every projection of a 7B-style block (4096
+    tokens) and a 65B-style block (2048 tokens), rank 64, s = 2, and the
+    blockwise NF4 + double-quant of all seven 65B-style tensors.  Weights come
+    from a seeded device generator with the workload's standard deviation;
+    activations and adapters likewise.  Eager launches timed with events (a
+    step is milliseconds, so launch cost is small)."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    out = {}
+    for name in ("block_7b", "block_65b"):
+        wl = synth.WORKLOADS[name]
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(1000 + wl.wid)
+        M, r, s = wl.M, wl.r, wl.s
+        layers, flops, quant_bytes, n_total = [], 0, 0, 0
+        Ws = []
+        for p in wl.projs:
+            W = torch.empty((p.o, p.d), dtype=torch.float32, device=dev).normal_(0.0, wl.w_std, generator=gen)
+            Ws.append(W)
+            n_total += W.numel()
+            c, s8, s2 = qb.qlora_quant_sizes(W.numel())
+            quant_bytes += 4 * W.numel() + c + s8 + s2
+        qs = [qb.qlora_quantize_nf4_dq(W, check_finite=False) for W in Ws]
+        torch.cuda.synchronize()
+        res = {"M": M, "r": r, "s": s, "projections": [f"{p.name} {p.o}x{p.d}" for p in wl.projs]}
+        if name == "block_65b":
+            # quantize of all seven tensors: fp32 read once, codes and scales written
+            for _ in range(2):
+                for W, q in zip(Ws, qs):
+                    qb.qlora_quantize_nf4_dq(W, check_finite=False, out=q)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(steps):
+                for W, q in zip(Ws, qs):
+                    qb.qlora_quantize_nf4_dq(W, check_finite=False, out=q)
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / steps
+            res["quantize_all"] = {"us": round(us, 1), "weights": n_total, "bytes": quant_bytes,
+                                   "GBps": round(quant_bytes / (us * 1e-6) / 1e9, 1),
+                                   "frac_of_hbm": round(quant_bytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)}
+        del Ws
+        ws_f, ws_b = qb.Workspace(), qb.Workspace()
+        for p, q in zip(wl.projs, qs):
+            X = torch.empty((M, p.d), device=dev).normal_(0.0, 1.0, generator=gen).to(torch.bfloat16)
+            dY = torch.empty((M, p.o), device=dev).normal_(0.0, 1.0, generator=gen).to(torch.bfloat16)
+            A = torch.empty((p.d, r), device=dev).normal_(0.0, 0.02, generator=gen).to(torch.bfloat16)
+            B = torch.empty((r, p.o), device=dev).normal_(0.0, 0.02, generator=gen).to(torch.bfloat16)
+            Y = torch.empty((M, p.o), dtype=torch.bfloat16, device=dev)
+            layers.append((q, X, dY, A, B, Y))
+            flops += step_flops(M, p.d, p.o, r)
+
+        def step():
+            for q, X, dY, A, B, Y in layers:
+                _, T = qb.qlora_linear_fwd(X, q, A, B, s, ws=ws_f, out=Y)
+                qb.qlora_linear_bwd(dY, X, T, q, A, B, s, ws=ws_b)
+
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        # the fused GEMM's share, from a separate step with per-launch events
+        qb.qlora_timing_begin([qb.K_MAIN_GEMM])
+        step()
+        torch.cuda.synchronize()
+        qb.qlora_timing_end()
+        gms, gn = qb.qlora_timing_read(qb.K_MAIN_GEMM)
+        res.update({"step": "fwd + bwd (dX, dA, dB) of every projection", "flop_per_step": flops,
+                    "ms_per_step": round(ms, 4), "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 2),
+                    "frac_of_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                    "main_gemm_ms_per_step": round(gms, 4), "main_gemm_launches_per_step": gn})
+        out[name] = res
+        del layers, qs
+        torch.cuda.empty_cache()
+    return out
 
 
 def optimizer_study(qb, torch, synth, dev):
