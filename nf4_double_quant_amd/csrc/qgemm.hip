@@ -421,24 +421,42 @@ __global__ __launch_bounds__(64 * kWaves) void k_qgemm(QGemmArgs p) {
     }
   }
 
-  // ---- epilogue: lane holds output row m = lane%32 of each 32×32 block and
-  // columns 8(e/4) + 4(lane/32) + e%4: four consecutive columns per 8-byte store
-  const Rsrc rcout = rsrc(p.C + m0 * p.ldc, (int64_t)mrows * p.ldc * 2);
+  // ---- epilogue.  Lane holds output row m = lane%32 of each 32×32 block and
+  // columns 8(e/4) + 4(lane/32) + e%4 (four consecutive columns per register
+  // quad).  Stored directly that would be 16-byte pieces of 32 rows per
+  // instruction; instead each wave puts its kWR×128 block, rounded to bf16,
+  // into its own part of the idle activation stages (256-byte rows, 16-byte
+  // chunks XOR-swizzled by row % 16 so the row-wise reads are conflict-free)
+  // and writes it back as whole rows: 4 rows × 256 bytes per instruction.
+  __syncthreads();   // every wave is done with the stages
+  static_assert(kWaves * kWR * kBN <= 2 * kBM * kBK, "the output block fits the two stages");
+  const int stage_off = wq * kWR * kBN;          // bf16 elements
+  uint16_t* st_out = stage_off < kBM * kBK ? sA0 + stage_off : sA1 + (stage_off - kBM * kBK);
 #pragma unroll
   for (int i = 0; i < kI; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int row = wq * kWR + i * 32 + (lane & 31);
-        const int64_t col = n0 + j * 32 + q * 8 + (lane >> 5) * 4;
-        const uint32_t off = col < p.N ? (uint32_t)((row * p.ldc + col) * 2) : kOobOff;
-        const uint32_t lo = pack_bf16x2(acc[i][j][4 * q + 0], acc[i][j][4 * q + 1]);
-        const uint32_t hi = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-        typedef int i32x2 __attribute__((ext_vector_type(2)));
-        const i32x2 val = {(int)lo, (int)hi};
-        __builtin_amdgcn_raw_buffer_store_b64(val, rcout, (int)off, 0, 0);
+        const int r = i * 32 + (lane & 31), c = 4 * j + q;
+        const uint2 v = make_uint2(pack_bf16x2(acc[i][j][4 * q + 0], acc[i][j][4 * q + 1]),
+                                   pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]));
+        *reinterpret_cast<uint2*>(st_out + r * kBN + ((c ^ (r & 15)) << 3) + (lane >> 5) * 4) = v;
       }
+  // the wave reads back only what its own lanes wrote
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const Rsrc rcout = rsrc(p.C + m0 * p.ldc, (int64_t)mrows * p.ldc * 2);   // rows past M: dropped
+#pragma unroll 8
+  for (int t = 0; t < kWR / 4; ++t) {
+    const int r = 4 * t + (lane >> 4), c = lane & 15;
+    const uint4 v = *reinterpret_cast<const uint4*>(st_out + r * kBN + ((c ^ (r & 15)) << 3));
+    const int row = wq * kWR + r;
+    const int64_t col = n0 + 8 * c;              // N % 8 == 0: a chunk is all in or all out
+    const uint32_t off = col < p.N ? (uint32_t)((row * p.ldc + col) * 2) : kOobOff;
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), rcout, (int)off, 0, 0);
+  }
 }
 
 hipError_t launch_qgemm(bool trans_w, const uint16_t* A, int64_t lda, const uint8_t* codes,
