@@ -242,12 +242,15 @@ __global__ __launch_bounds__(64 * kWaves) void k_qgemm(QGemmArgs p) {
   };
 
   f32x16 acc[kI][4];
+  // zeroed while the first k-step's loads are in flight (256 AGPR writes)
+  auto zero_acc = [&]() {
 #pragma unroll
-  for (int i = 0; i < kI; ++i)
+    for (int i = 0; i < kI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+  };
 
   // Fragments of one 16-wide k sub-step: kI activation row blocks × 4 weight
   // column blocks.  kBTr: the weight-side tile is [k][n] (read transposed).
@@ -325,6 +328,12 @@ __global__ __launch_bounds__(64 * kWaves) void k_qgemm(QGemmArgs p) {
     dma_a(Unchecked{}, a_base, lda2b, 0, p.K, sA0);
     load_codes(0, r0);
     load_codes(1, r1);
+    zero_acc();
+    // pin the zeroing here: otherwise it sinks past the first barrier
+#pragma unroll
+    for (int i = 0; i < kI; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) asm volatile("" : "+a"(acc[i][j]));
     expand_block(r0, sB0);
     __builtin_amdgcn_s_waitcnt(kWaitAll);
     __syncthreads();
@@ -372,6 +381,8 @@ __global__ __launch_bounds__(64 * kWaves) void k_qgemm(QGemmArgs p) {
       iteration(std::true_type{}, s + 1, r1, r0);
     }
     if (s < nkf) iteration(std::false_type{}, s, r0, r1);
+  } else {
+    zero_acc();
   }
   // ---- the partial last k-step (K % 64 != 0): weight rows past K read 0
   if (nkf * kBK < p.K) {
