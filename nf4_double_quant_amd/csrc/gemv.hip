@@ -218,7 +218,7 @@ __host__ __device__ inline GemvSmem gemv_smem(int nw, int mx, int M, int r, int 
                                               bool t_regs) {
   GemvSmem s;
   int off = 0;
-  s.x = off;    off += mx <= 4 ? nw * (mx + 1) * 36 * 16 : 0; // staged activations + a zero row
+  s.x = off;    off += nw * (mx + 1) * 36 * 16;              // staged activations + a zero row
   s.part = off; off += nw * 16 * 17 * 4;                      // per-wave partial sums
   s.tp = off;   off += t_regs ? tplanes * M * r * 4 : 0;      // T planes (register path)
   s.t = off;    off += M * r * 4;                             // T = X·A
@@ -232,16 +232,20 @@ __host__ __device__ inline GemvSmem gemv_smem(int nw, int mx, int M, int r, int 
 // host picks nw = ceil(groups / 4) up to kGemvMaxWaves, so for d <= 12288
 // every wave owns at most four groups and issues all its loads at once.
 //
-// MX (the largest M the instance serves) selects how the activations reach
-// the MFMA A operand.  The operand lane (m, q) needs the 128 bytes of row m
-// under its block.  For MX <= 4 the wave loads the group's M×512 bytes with
-// ceil(M/2) 16-byte loads and redistributes them through a wave-private LDS
-// tile; for larger M every operand lane loads its 128 bytes itself.
+// The activations reach the MFMA A operand through a wave-private LDS
+// tile: the operand lane (m, q) needs the 128 bytes of row m under its
+// block, while the wave loads the group's M×512 bytes as whole 1 KB runs
+// (ceil(M/2) 16-byte loads per lane; MX, the largest M the instance serves,
+// sizes the tile) and redistributes them.  For MX <= 4 four groups of codes
+// and activations are in flight; the 16-token instance keeps activations
+// one group ahead and, holding 8 staged chunks per lane, runs at most 8
+// waves with more registers each.
+__host__ __device__ constexpr int gemv_max_waves(int mx) { return mx == 16 ? 8 : kGemvMaxWaves; }
+
 template <int MX>
-__global__ __launch_bounds__(kGemvMaxWaves * 64) void k_gemv(GemvArgs p) {
+__global__ __launch_bounds__(gemv_max_waves(MX) * 64) void k_gemv(GemvArgs p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  constexpr bool kStage = MX <= 4;
-  constexpr int kNX = kStage ? (MX * 32 + 63) / 64 : 8;     // activation loads per lane per group
+  constexpr int kNX = (MX * 32 + 63) / 64;                  // activation loads per lane per group
   constexpr int kXRow = 36;                                 // staged row: 4 blocks × (8 + 1 pad) uint4
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int nw = (int)(blockDim.x >> 6), nthr = (int)blockDim.x;
@@ -299,9 +303,7 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void k_gemv(GemvArgs p) {
     }
   }
 
-  if constexpr (kStage) {
-    if (lane < kXRow) s_x[MX * kXRow + lane] = make_uint4(0, 0, 0, 0);
-  }
+  if (lane < kXRow) s_x[MX * kXRow + lane] = make_uint4(0, 0, 0, 0);
   const bool row_ok = n < p.o;
   const uint32_t brow = row_ok ? (uint32_t)n * nblk : 0u;
   // the 8-bit scale of block b is byte b%4 of dword b/4; b%4 = (brow + q)%4
@@ -322,50 +324,37 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void k_gemv(GemvArgs p) {
     c.step = __builtin_bit_cast(
         float, __builtin_amdgcn_raw_buffer_load_b32(rs2, (int)(ok ? (b / kGroup) * 4 : kGOob), 0, 0));
   };
-  // activations of slot `it`: staged layout (chunk c = u·64 + lane holds
-  // row c/32, 8 values at k = 8·(c%32) of the group) or operand layout
+  // activations of slot `it` in the staged layout: chunk c = u·64 + lane
+  // holds row c/32, 8 values at k = 8·(c%32) of the group (1 KB per load)
   auto load_x = [&](int it, uint4 (&x)[kNX]) {
     const uint32_t g = group_of(it);
 #pragma unroll
     for (int u = 0; u < kNX; ++u) {
-      uint32_t off;
-      bool ok;
-      if constexpr (kStage) {
-        const int c = u * 64 + lane, mm = c >> 5, kc = c & 31;
-        ok = mm < p.M && g * 4 + (kc >> 3) < nblk;
-        off = ((uint32_t)mm * (uint32_t)p.d + g * 256 + kc * 8) * 2;
-      } else {
-        const uint32_t kb = g * 4 + q;
-        ok = m < p.M && kb < nblk;
-        off = ((uint32_t)m * (uint32_t)p.d + kb * kBlock) * 2 + 16 * u;
-      }
+      const int c = u * 64 + lane, mm = c >> 5, kc = c & 31;
+      const bool ok = mm < p.M && g * 4 + (kc >> 3) < nblk;
+      const uint32_t off = ((uint32_t)mm * (uint32_t)p.d + g * 256 + kc * 8) * 2;
       x[u] = gload16(rx, ok ? off : kGOob);
     }
   };
   // staged activations -> operand layout, through this wave's LDS tile
   // (row stride and a pad after every block make the reads conflict-free)
   auto operands = [&](const uint4 (&x)[kNX], uint4 (&xa)[8]) {
-    if constexpr (kStage) {
 #pragma unroll
-      for (int u = 0; u < kNX; ++u) {
-        const int c = u * 64 + lane, mm = c >> 5, kc = c & 31;
-        if (mm < MX) s_x[mm * kXRow + kc + (kc >> 3)] = x[u];
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      // operand rows m >= M read zeros: rows M..MX-1 were staged from
-      // out-of-range loads, and row MX is the zero row
-      const int mr = m < MX ? m : MX;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) xa[j] = s_x[mr * kXRow + q * 9 + j];
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) xa[j] = x[j];
+    for (int u = 0; u < kNX; ++u) {
+      const int c = u * 64 + lane, mm = c >> 5, kc = c & 31;
+      if (mm < MX) s_x[mm * kXRow + kc + (kc >> 3)] = x[u];
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // operand rows m >= M read zeros: rows M..MX-1 were staged from
+    // out-of-range loads, and row MX is the zero row
+    const int mr = m < MX ? m : MX;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) xa[j] = s_x[mr * kXRow + q * 9 + j];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
   f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
   auto compute = [&](const GemvCodes& c, const uint4 (&x)[kNX]) {
@@ -385,7 +374,7 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void k_gemv(GemvArgs p) {
   // the one held, and the last four slots are computed after it with no
   // further loads (slots past niter hold zeros).
   GemvCodes c0, c1, c2, c3;
-  if constexpr (kStage) {
+  if constexpr (MX <= 4) {
     uint4 x0[kNX], x1[kNX], x2[kNX], x3[kNX];
     // (the scheduling barriers keep each group's loads together, in order,
     // so that the wait for a group never covers a later one)
@@ -515,13 +504,17 @@ GemvPlan gemv_plan(int M, int64_t d, int r, bool lora, bool want_t) {
   GemvPlan g{};
   const int64_t nblk = d / kBlock;
   const int64_t chunks = (nblk + 15) / 16;
-  g.nw = (int)std::min<int64_t>(kGemvMaxWaves, std::max<int64_t>(1, chunks));
   g.mx = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 16;
   g.rr = r;
   const int ts = gemv_tsplits(d);
-  g.t_regs = want_t && (int64_t)ts * M * r <= 4 * g.nw * 64;
-  if (g.t_regs && gemv_smem(g.nw, g.mx, M, r, ts, true).bytes > kGemvMaxLds) g.t_regs = false;
-  g.lds = gemv_smem(g.nw, g.mx, M, r, ts, g.t_regs).bytes;
+  // as many waves as four-group chunks, up to kGemvMaxWaves, fewer when the
+  // staged activations of that many waves would not fit the shared memory
+  for (g.nw = (int)std::min<int64_t>(gemv_max_waves(g.mx), std::max<int64_t>(1, chunks)); ; --g.nw) {
+    g.t_regs = want_t && (int64_t)ts * M * r <= 4 * g.nw * 64;
+    if (g.t_regs && gemv_smem(g.nw, g.mx, M, r, ts, true).bytes > kGemvMaxLds) g.t_regs = false;
+    g.lds = gemv_smem(g.nw, g.mx, M, r, ts, g.t_regs).bytes;
+    if (g.lds <= kGemvMaxLds || g.nw == 1) break;
+  }
   (void)lora;
   return g;
 }
