@@ -342,8 +342,9 @@ __global__ __launch_bounds__(64 * kWaves) void k_qgemm(QGemmArgs p) {
     // s+2 go out with the second share and get most of a step), expand code words
     // of s+1 into the idle weight buffer and issue the MFMAs, DMA instructions
     // interleaved with MFMAs so the address FIFO never backs up and stalls the
-    // wave; then wait for the DMA and publish.  Loads for steps at or past nkf
-    // land in the idle buffers and are never used.
+    // wave; then publish the weight tile.  Loads for steps at or past nkf
+    // land in the idle buffers and are never used (the barriers after the
+    // loop wait for them).
     auto iteration = [&](auto stage, int s, Codes& refill, const Codes& next) {
       constexpr bool kOdd = decltype(stage)::value;
       uint16_t* a_cur = kOdd ? sA1 : sA0;
@@ -351,6 +352,8 @@ __global__ __launch_bounds__(64 * kWaves) void k_qgemm(QGemmArgs p) {
       uint16_t* b_cur = kOdd ? sB1 : sB0;
       uint16_t* b_nxt = kOdd ? sB0 : sB1;
       Frags f[2];
+      // this wave's own activation rows of step s (its DMA) are in
+      __builtin_amdgcn_s_waitcnt(kWaitAll);
       read_frags(WTag{}, f[0], a_cur, b_cur, 0);
       __builtin_amdgcn_sched_barrier(0);
       Lut lut;
@@ -372,8 +375,10 @@ __global__ __launch_bounds__(64 * kWaves) void k_qgemm(QGemmArgs p) {
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_s_waitcnt(kWaitAll);
-      lds_barrier();
+      // publish the expanded weight tile of step s+1 (LDS writes only: each
+      // wave's activation rows are its own, and it waits for their DMA at the
+      // top of the next step; a fence here would wait for the DMA as well)
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     };
     int s = 0;
     for (; s + 1 < nkf; s += 2) {
