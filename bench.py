@@ -373,6 +373,42 @@ def bench_decode(args, qb, torch, np, synth, dev):
 
         res[f"M{M}"] = _time_decode(qb, torch, sets, one, ys, byts, K_GEMV=qb.K_GEMV)
 
+    # gate and up read the same input in an MLP: run them as one projection of
+    # 22016 rows with the two adapters side by side (A = [A_gate | A_up], B
+    # block-diagonal), which gives the same outputs with two launches fewer
+    P = {p.name: p for p in wl.projs}
+    g_, u_, dn_ = P["gate"], P["up"], P["down"]
+    fused_sets = []
+    for layer in sets:
+        qs = {p.name: qw for p, qw in layer}
+        fused_sets.append((qb.qlora_stack_rows([qs["gate"], qs["up"]]), qs["down"]))
+    Ag, Bg = adapters["gate"]
+    Au, Bu = adapters["up"]
+    A_gu = torch.cat([Ag, Au], 1).contiguous()
+    B_gu = torch.zeros((2 * wl.r, g_.o + u_.o), dtype=torch.bfloat16, device=dev)
+    B_gu[:wl.r, :g_.o] = Bg
+    B_gu[wl.r:, g_.o:] = Bu
+    for M in (1, 4, 16):
+        x = torch.from_numpy(synth.normal_bf16((M, g_.d), 1.0, [wl.wid, synth.PROJ_IDS["gate"], synth.T_X])
+                             .view(np.int16)).view(torch.bfloat16).to(dev)
+        h = torch.from_numpy(synth.normal_bf16((M, dn_.d), 1.0, [wl.wid, synth.PROJ_IDS["down"], synth.T_X])
+                             .view(np.int16)).view(torch.bfloat16).to(dev)
+        ys = {"gate_up": torch.empty((M, g_.o + u_.o), dtype=torch.bfloat16, device=dev),
+              "down": torch.empty((M, dn_.o), dtype=torch.bfloat16, device=dev)}
+        byts = 0
+        for p in wl.projs:
+            c, s8, s2 = qb.qlora_quant_sizes(p.o * p.d)
+            byts += c + s8 + s2 + 2 * (p.d * wl.r + wl.r * p.o + M * p.o)
+        byts += 2 * M * (g_.d + dn_.d)               # x once for gate and up, h for down
+        Ad, Bd = adapters["down"]
+
+        def one_fused(layer):
+            qgu, qd = layer
+            qb.qlora_linear_fwd(x, qgu, A_gu, B_gu, wl.s, want_T=False, ws=ws, out=ys["gate_up"])
+            qb.qlora_linear_fwd(h, qd, Ad, Bd, wl.s, want_T=False, ws=ws, out=ys["down"])
+
+        res[f"M{M}_gate_up_fused"] = _time_decode(qb, torch, fused_sets, one_fused, ys, byts, K_GEMV=qb.K_GEMV)
+
     # one adapter per token: 16 tokens on 16 different rank-16 adapters per projection
     M, n_ad = 16, 16
     multi_ad = {p.name: (bfd(synth.normal_bf16((n_ad, p.d, wl.r), 0.02, [wl.wid, synth.PROJ_IDS[p.name], synth.T_A_STACK])),
@@ -396,6 +432,8 @@ def bench_decode(args, qb, torch, np, synth, dev):
 
     res["M16_16_adapters"] = _time_decode(qb, torch, sets, one_multi, ys, byts, K_GEMV=qb.K_GEMV)
     return {"workload": "decode_mlp_7b: gate/up 4096->11008, down 11008->4096, r=16, fwd only; "
+                        "M*_gate_up_fused: gate and up share their input and run as one 22016-row "
+                        "projection (adapters side by side, B block-diagonal); "
                         "M16_16_adapters: one adapter per token (16 adapters per projection)",
             "weight_sets_cycled": len(sets), "peak_GBps": PEAK_HBM_GBPS, **res}
 

@@ -24,6 +24,7 @@ LIB_PATH = os.path.join(_PKG, "libqlora.so")
 QLORA_OK, QLORA_E_NONFINITE = 0, 7
 QLORA_F32, QLORA_BF16 = 0, 1
 QLORA_OP_FWD, QLORA_OP_BWD = 0, 1
+QLORA_BLOCK, QLORA_GROUP = 64, 256     # weights per block, blocks per double-quant group
 # Tables of the 4-bit codes (qlora_fmt) and codes of the constants (qlora_dq).
 FORMATS = {"nf4": 0, "int4": 1, "fp4_e2m1": 2, "fp4_e3m0": 3}
 DQ_VARIANTS = {"uint8": 0, "int8_mean": 1, "fp8_mean": 2}
@@ -255,6 +256,30 @@ def qlora_quantize_nf4_dq(W, check_finite: bool = True, out: QuantizedWeight | N
         raise QloraError(QLORA_E_NONFINITE, "qlora_quantize_nf4_dq")
     q.flags = flags
     return q
+
+
+def qlora_stack_rows(parts) -> QuantizedWeight:
+    """Quantized weights of one row length stacked by rows into one quantized
+    tensor, e.g. projections that read the same input run as one layer.  The
+    result is exactly what quantizing the stacked fp32 rows gives, which holds
+    when every part covers whole double-quant groups (16384 weights), so that
+    no group spans two parts; other parts raise ValueError.  Buffer copies only."""
+    torch = _torch()
+    parts = list(parts)
+    if not parts:
+        raise ValueError("no parts")
+    d = parts[0].shape[-1]
+    for q in parts:
+        if q.n % (QLORA_BLOCK * QLORA_GROUP) != 0:
+            raise ValueError("each part must hold whole double-quant groups (16384 weights)")
+        if q.shape[-1] != d or q.fmt != parts[0].fmt or q.dq != 0 or parts[0].dq != 0:
+            raise ValueError("parts need one row length, one code table and the default second level")
+    sizes = [qlora_quant_sizes(q.n) for q in parts]
+    codes = torch.cat([q.codes[:c] for q, (c, _, _) in zip(parts, sizes)])
+    scale8 = torch.cat([q.scale8[:s8] for q, (_, s8, _) in zip(parts, sizes)])
+    scale2 = torch.cat([q.scale2[:s2 // 4] for q, (_, _, s2) in zip(parts, sizes)])
+    rows = sum(q.n // d for q in parts)
+    return QuantizedWeight(codes, scale8, scale2, sum(q.n for q in parts), (rows, d), parts[0].fmt, 0)
 
 
 def qlora_dequant(q: QuantizedWeight, dtype=None):

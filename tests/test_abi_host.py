@@ -213,3 +213,31 @@ def test_no_device_status(L):
                               A16, 1 << 30, None) == 5
     # size-0 work is a no-op even without a device
     assert L.qlora_quantize_nf4_dq(A16, 0, ctypes.byref(_view(0)), None, None) == 0
+
+
+def test_stack_rows_layout_and_checks():
+    """qlora_stack_rows concatenates codes, 8-bit scales and steps in order
+    (buffer copies, checked here on host tensors) and refuses parts that do
+    not hold whole double-quant groups or differ in row length."""
+    torch = pytest.importorskip("torch")
+
+    def part(rows, d, seed):
+        n = rows * d
+        c, s8, s2 = qb.qlora_quant_sizes(n)
+        g = torch.Generator().manual_seed(seed)
+        return qb.QuantizedWeight(torch.randint(0, 256, (c,), dtype=torch.uint8, generator=g),
+                                  torch.randint(0, 256, (s8,), dtype=torch.uint8, generator=g),
+                                  torch.rand(s2 // 4, generator=g), n, (rows, d))
+
+    a, b = part(64, 256, 1), part(128, 256, 2)
+    st = qb.qlora_stack_rows([a, b])
+    assert st.n == a.n + b.n and st.shape == (192, 256)
+    assert torch.equal(st.codes, torch.cat([a.codes, b.codes]))
+    assert torch.equal(st.scale8, torch.cat([a.scale8, b.scale8]))
+    assert torch.equal(st.scale2, torch.cat([a.scale2, b.scale2]))
+    with pytest.raises(ValueError):
+        qb.qlora_stack_rows([a, part(65, 256, 3)])          # 16640 weights: a partial group
+    with pytest.raises(ValueError):
+        qb.qlora_stack_rows([a, part(128, 128, 4)])         # another row length
+    with pytest.raises(ValueError):
+        qb.qlora_stack_rows([])

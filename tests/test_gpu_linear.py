@@ -231,3 +231,33 @@ def test_workspace_reuse_across_shapes():
         outs.append((Y.clone(), dX.clone(), dA.clone(), dB.clone()))
     for a, b in zip(outs[0], outs[2]):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("M", [3, 40])
+def test_stacked_projections_match_separate_calls(M):
+    """Two projections of one input stacked by rows (qlora_stack_rows) with
+    their adapters side by side (A = [A1 | A2], B block-diagonal) give the
+    same bits as two separate layers, on the few-token and the GEMM path.
+    The stacked codes and scales are those of quantizing the stacked rows."""
+    d, o1, o2, r, s = 256, 64, 128, 8, 2.0
+    W1 = synth.normal_f32((o1, d), 0.02, [81, 0, 0])
+    W2 = synth.normal_f32((o2, d), 0.02, [81, 1, 0])
+    X = bf16_dev(synth.normal_bf16((M, d), 1.0, [81, 2, 0]))
+    A1, A2 = (bf16_dev(synth.normal_bf16((d, r), 0.02, [81, 3, k])) for k in range(2))
+    B1 = bf16_dev(synth.normal_bf16((r, o1), 0.02, [81, 4, 0]))
+    B2 = bf16_dev(synth.normal_bf16((r, o2), 0.02, [81, 4, 1]))
+    q1 = qb.qlora_quantize_nf4_dq(torch.from_numpy(W1).cuda())
+    q2 = qb.qlora_quantize_nf4_dq(torch.from_numpy(W2).cuda())
+    qs = qb.qlora_stack_rows([q1, q2])
+    qw = qb.qlora_quantize_nf4_dq(torch.from_numpy(np.concatenate([W1, W2])).cuda())
+    for a, b in ((qs.codes, qw.codes), (qs.scale8, qw.scale8), (qs.scale2, qw.scale2)):
+        assert torch.equal(a[: b.numel()], b)
+    A = torch.cat([A1, A2], 1).contiguous()
+    B = torch.zeros((2 * r, o1 + o2), dtype=torch.bfloat16, device="cuda")
+    B[:r, :o1], B[r:, o1:] = B1, B2
+    Y, _ = qb.qlora_linear_fwd(X, qs, A, B, s)
+    Y1, _ = qb.qlora_linear_fwd(X, q1, A1, B1, s)
+    Y2, _ = qb.qlora_linear_fwd(X, q2, A2, B2, s)
+    torch.cuda.synchronize()
+    # +0 terms of the block-diagonal B leave every sum unchanged (up to the sign of zero)
+    assert torch.equal(Y[:, :o1].float(), Y1.float()) and torch.equal(Y[:, o1:].float(), Y2.float())
