@@ -357,9 +357,8 @@ __global__ __launch_bounds__(gemv_max_waves(MX) * 64) void k_gemv(GemvArgs p) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
   f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  auto compute = [&](const GemvCodes& c, const uint4 (&x)[kNX]) {
-    uint4 xa[8];
-    operands(x, xa);
+  // one group: the block's table, its 64 codes expanded, 8 MFMAs
+  auto compute_ops = [&](const GemvCodes& c, const uint4 (&xa)[8]) {
     Lut lut;
     const float q8 = (float)__builtin_amdgcn_ubfe(c.q8, sh8, 8);
     build_lut(p.cb, q8 * c.step, lut);            // ĉ = fl32(q8·step)
@@ -369,10 +368,16 @@ __global__ __launch_bounds__(gemv_max_waves(MX) * 64) void k_gemv(GemvArgs p) {
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa[j]), expand8(lut, cw[j]),
                                                     acc, 0, 0, 0);
   };
+  auto compute = [&](const GemvCodes& c, const uint4 (&x)[kNX]) {
+    uint4 xa[8];
+    operands(x, xa);
+    compute_ops(c, xa);
+  };
 
   // Four groups of codes in flight; the loop runs while more chunks follow
   // the one held, and the last four slots are computed after it with no
-  // further loads (slots past niter hold zeros).
+  // further loads (slots past niter hold zeros; branching around them costs
+  // more than the few wasted ones).
   GemvCodes c0, c1, c2, c3;
   if constexpr (MX <= 4) {
     uint4 x0[kNX], x1[kNX], x2[kNX], x3[kNX];
@@ -394,22 +399,44 @@ __global__ __launch_bounds__(gemv_max_waves(MX) * 64) void k_gemv(GemvArgs p) {
     compute(c2, x2);
     compute(c3, x3);
   } else {
-    // activations one group ahead
-    uint4 xa[8], xb[8];
-    load_codes(0, c0); __builtin_amdgcn_sched_barrier(0);
-    load_x(0, xa); __builtin_amdgcn_sched_barrier(0);
-    load_codes(1, c1); load_codes(2, c2); load_codes(3, c3); __builtin_amdgcn_sched_barrier(0);
-    int it = 0;
-    for (; it + 4 < niter; it += 4) {
-      load_x(it + 1, xb); compute(c0, xa); load_codes(it + 4, c0);
-      load_x(it + 2, xa); compute(c1, xb); load_codes(it + 5, c1);
-      load_x(it + 3, xb); compute(c2, xa); load_codes(it + 6, c2);
-      load_x(it + 4, xa); compute(c3, xb); load_codes(it + 7, c3);
+    // 16 tokens: the tile takes a group's activations as soon as they
+    // arrive, so registers hold only the next group's chunks (one group
+    // ahead) besides the operands in use, and codes run two groups ahead;
+    // that keeps three waves per SIMD.  Rows of the tile are rewritten only
+    // after this wave's reads of the previous group (its LDS operations run
+    // in order).
+    uint4 xn[kNX];
+    auto stage_write = [&]() {
+#pragma unroll
+      for (int u = 0; u < kNX; ++u) {
+        const int c = u * 64 + lane, mm = c >> 5, kc = c & 31;
+        s_x[mm * kXRow + kc + (kc >> 3)] = xn[u];
+      }
+    };
+    auto stage_read = [&](uint4 (&xa)[8]) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int j = 0; j < 8; ++j) xa[j] = s_x[m * kXRow + q * 9 + j];
+    };
+    auto step = [&](int it, GemvCodes& c) {
+      uint4 xa[8];
+      stage_read(xa);                  // group it
+      stage_write();                   // group it + 1
+      load_x(it + 2, xn);
+      compute_ops(c, xa);
+      load_codes(it + 2, c);
+    };
+    load_codes(0, c0); load_x(0, xn); __builtin_amdgcn_sched_barrier(0);
+    load_codes(1, c1); __builtin_amdgcn_sched_barrier(0);
+    stage_write();
+    load_x(1, xn);
+    for (int it = 0; it < niter; it += 2) {
+      step(it, c0);
+      if (it + 1 >= niter) break;
+      step(it + 1, c1);
     }
-    load_x(it + 1, xb); compute(c0, xa);
-    load_x(it + 2, xa); compute(c1, xb);
-    load_x(it + 3, xb); compute(c2, xa);
-    compute(c3, xb);
   }
 
   // ---- epilogue: Y = Σ partials + s·T·B
