@@ -18,8 +18,10 @@
 //  * Exact nearest-value encode without fp64 per weight: for each block the
 //    15 decision points c1·mid_t are exact fp64 products; rounding each one
 //    DOWN to fp32 gives a threshold th_t with  w > c1·mid_t  <=>  w > th_t
-//    for every fp32 w.  A thread per block builds them once; each weight
-//    then takes a 4-level branch-free binary search in fp32.
+//    for every fp32 w.  A thread per block builds them once, as unsigned
+//    keys with the order of the fp32 values, into shared memory; each weight
+//    then takes a 4-level binary search that reads one threshold per level
+//    and shifts the comparison's borrow into the code (two VALU operations).
 //  * Codes are packed 8 per 32-bit word (byte j = code j | code j+4 << 4):
 //    the two lanes holding a word's halves merge them with one shuffle, the
 //    words are gathered in LDS and written out as 16-byte stores.
@@ -37,17 +39,19 @@ __device__ __forceinline__ float round_down_f32(double p) {
   return f;
 }
 
-// Number of thresholds strictly below w (= the NF4 code); thresholds
-// t0..t14 ascending in a.x..d.z.  A 4-level search on register values.
-__device__ __forceinline__ uint32_t nf4_search(float w, float4 a, float4 b, float4 c, float4 d) {
-  const bool b3 = w > b.w;                                   // t7
-  const bool b2 = w > (b3 ? c.w : a.w);                      // t11 | t3
-  const float t1 = b3 ? (b2 ? d.y : c.y) : (b2 ? b.y : a.y); // t13 t9 t5 t1
-  const bool b1 = w > t1;
-  const float lo = b1 ? (b2 ? b.z : a.z) : (b2 ? b.x : a.x); // t6 t2 t4 t0
-  const float hi = b1 ? (b2 ? d.z : c.z) : (b2 ? d.x : c.x); // t14 t10 t12 t8
-  const bool b0 = w > (b3 ? hi : lo);
-  return ((uint32_t)b3 << 3) | ((uint32_t)b2 << 2) | ((uint32_t)b1 << 1) | (uint32_t)b0;
+// Unsigned key with the order of the fp32 values (-0 just below +0): for the
+// thresholds used here, none of them -0, k(w) > k(t) exactly when w > t.
+__device__ __forceinline__ uint32_t order_key(float x) {
+  const uint32_t b = __float_as_uint(x);
+  return b ^ ((uint32_t)((int32_t)b >> 31) | 0x80000000u);
+}
+
+// 2k + (t < u): the borrow of t - u carried into k + k (two VALU operations)
+__device__ __forceinline__ uint32_t bit_in(uint32_t k, uint32_t t, uint32_t u) {
+  uint32_t d, r;
+  asm("v_sub_co_u32 %0, vcc, %2, %3\n\tv_addc_co_u32 %1, vcc, %4, %4, vcc"
+      : "=&v"(d), "=v"(r) : "v"(t), "v"(u), "v"(k) : "vcc");
+  return r;
 }
 
 // max over the 16 lanes of a DPP row (rotations by 8, 4, 2, 1)
@@ -74,7 +78,7 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, i
                                                   uint8_t* __restrict__ scale8,
                                                   float* __restrict__ scale2,
                                                   int32_t* __restrict__ flags, Codebook cb) {
-  __shared__ __attribute__((aligned(16))) float4 s_thr[kGroup][4];
+  __shared__ __attribute__((aligned(16))) uint32_t s_thr[kGroup][16];   // threshold order keys
   __shared__ __attribute__((aligned(16))) uint32_t s_codes[kGroupElems / 8];
   __shared__ uint32_t s_c1[kGroup];
   __shared__ uint32_t s_red[4];
@@ -142,10 +146,8 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, i
       for (int i = 0; i < 15; ++i) th[i] = round_down_f32((double)c1 * cb.mid[i]);
       th[15] = 0.0f;
     }
-    s_thr[t][0] = make_float4(th[0], th[1], th[2], th[3]);
-    s_thr[t][1] = make_float4(th[4], th[5], th[6], th[7]);
-    s_thr[t][2] = make_float4(th[8], th[9], th[10], th[11]);
-    s_thr[t][3] = make_float4(th[12], th[13], th[14], th[15]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s_thr[t][i] = order_key(th[i]);
   }
   __syncthreads();
 
@@ -153,11 +155,24 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, i
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     const int bl = wave * 64 + j * 4 + quad;
-    const float4 ta = s_thr[bl][0], tb = s_thr[bl][1], tc = s_thr[bl][2], td = s_thr[bl][3];
-    const uint32_t k0 = nf4_search(v[j].x, ta, tb, tc, td);
-    const uint32_t k1 = nf4_search(v[j].y, ta, tb, tc, td);
-    const uint32_t k2 = nf4_search(v[j].z, ta, tb, tc, td);
-    const uint32_t k3 = nf4_search(v[j].w, ta, tb, tc, td);
+    // binary search on order keys, level by level for the four weights:
+    // k collects the code bits from the top, and each level reads the one
+    // threshold it compares against (index 8k+3, 4k+1, 2k)
+    const uint32_t* T = s_thr[bl];
+    const uint32_t t7 = T[7];
+    const uint32_t u[4] = {order_key(v[j].x), order_key(v[j].y), order_key(v[j].z), order_key(v[j].w)};
+    uint32_t kk[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) kk[e] = bit_in(0u, t7, u[e]);
+#pragma unroll
+    for (int lev = 0; lev < 3; ++lev) {
+      uint32_t th[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) th[e] = T[lev == 0 ? 8 * kk[e] + 3 : lev == 1 ? 4 * kk[e] + 1 : 2 * kk[e]];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) kk[e] = bit_in(kk[e], th[e], u[e]);
+    }
+    const uint32_t k0 = kk[0], k1 = kk[1], k2 = kk[2], k3 = kk[3];
     // lane `sub` holds codes 4·sub..4·sub+3 of the block: low nibbles of a
     // word for even sub, high nibbles for odd sub; neighbours merge by DPP
     const uint32_t half = (k0 | (k1 << 8) | (k2 << 16) | (k3 << 24)) << ((sub & 1) * 4);
