@@ -247,6 +247,7 @@ def main():
 
     decode = None if args.no_decode else bench_decode(args, qb, torch, np, synth, dev)
     blocks = None if args.no_blocks else bench_blocks(qb, torch, synth, dev)
+    tiny = tiny_latency(qb, torch, np, synth, dev)
     formats = format_errors(qb, torch, W)
     merge_res = merge_study(qb, torch, W, q, X, A, B, s)
     optim = optimizer_study(qb, torch, synth, dev)
@@ -266,6 +267,7 @@ def main():
                    "parallelism": "single GPU"},
         "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "roofline": roofline, "breakdown": breakdown, "decode": decode, "blocks": blocks,
+        "tiny_latency": tiny,
         "formats": formats,
         "merge": merge_res, "optimizer": optim,
         "cpu_baseline": cpu,
@@ -565,6 +567,53 @@ def optimizer_study(qb, torch, synth, dev):
                          "frac_of_sequential_copies": round((us_h2d + us_d2h) / us_paged, 3)},
         "device_state_bytes_saved": 8 * n,
     }
+
+
+def tiny_latency(qb, torch, np, synth, dev, reps=200):
+    """Latency of one step (quantize + fwd + bwd) of the single 128×128
+    linear (8 tokens, rank 8): eager, and as a HIP-graph replay."""
+    wl = synth.WORKLOADS["tiny_128"]
+    p = wl.projs[0]
+    W_h, X_h, A_h, B_h, dY_h = synth.layer_inputs(wl, p)
+    bf = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
+    W = torch.from_numpy(W_h).to(dev)
+    X, A, B, dY = bf(X_h), bf(A_h), bf(B_h), bf(dY_h)
+    q = qb.qlora_quantize_nf4_dq(W)
+    Y = torch.empty((wl.M, p.o), dtype=torch.bfloat16, device=dev)
+    ws_f, ws_b = qb.Workspace(), qb.Workspace()
+
+    def step():
+        qb.qlora_quantize_nf4_dq(W, check_finite=False, out=q)
+        _, T = qb.qlora_linear_fwd(X, q, A, B, wl.s, ws=ws_f, out=Y)
+        qb.qlora_linear_bwd(dY, X, T, q, A, B, wl.s, ws=ws_b)
+
+    for _ in range(10):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    eager = e0.elapsed_time(e1) * 1e3 / reps
+    res = {"workload": "tiny_128: 128x128 linear, 8 tokens, r = 8, quantize + fwd + bwd",
+           "us_per_step_eager": round(eager, 2)}
+    try:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        g.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        res["us_per_step_graph"] = round(e0.elapsed_time(e1) * 1e3 / reps, 2)
+    except Exception as e:  # capture unsupported: the eager figure stands
+        print(f"tiny graph capture failed: {e}", file=sys.stderr)
+    return res
 
 
 def merge_study(qb, torch, W, q, X, A, B, s):
