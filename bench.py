@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-blocks", action="store_true",
                     help="skip the 7B / 65B-style block measurements")
+    ap.add_argument("--no-tiny", action="store_true",
+                    help="skip the 128x128 latency measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--pmc", action="store_true",
@@ -247,7 +249,7 @@ def main():
 
     decode = None if args.no_decode else bench_decode(args, qb, torch, np, synth, dev)
     blocks = None if args.no_blocks else bench_blocks(qb, torch, synth, dev)
-    tiny = tiny_latency(qb, torch, np, synth, dev)
+    tiny = None if args.no_tiny else tiny_latency(qb, torch, np, synth, dev)
     formats = format_errors(qb, torch, W)
     merge_res = merge_study(qb, torch, W, q, X, A, B, s)
     optim = optimizer_study(qb, torch, synth, dev)
