@@ -14,8 +14,11 @@
 // same bits as the standalone dequant), byte permutes, and 64 bytes of bf16
 // written to LDS.  The activation tile goes memory -> LDS directly
 // (buffer_load ... lds) one k-step ahead, its instructions spread between
-// the MFMAs; each wave loads exactly the 128 rows it multiplies.  Codes are
-// loaded one k-step ahead of their expansion.
+// the MFMAs; each wave loads exactly the 128 rows it multiplies, so the one
+// barrier per k-step publishes only the expanded weights and each wave
+// waits for its own DMA.  Codes are loaded one k-step ahead of their
+// expansion.  The finished block leaves through the idle activation stages
+// as whole 256-byte rows.
 //
 //  * forward: the weight tile is [n][k] like the activation tile (k-major
 //    rows, XOR-swizzled 16-byte chunks), read with ds_read_b128;
