@@ -222,7 +222,7 @@ int qlora_quantize_nf4_dq(const float* W, int64_t n, const qlora_nf4dq* out, int
   if (n == 0) return QLORA_OK;
   if ((st = device_status())) return st;
   QL_RUN(QLORA_K_QUANTIZE, (hipStream_t)stream, launch_quantize(W, n, out->codes, out->scale8, out->scale2, d_flags,
-                                                                   host_codebook(out->fmt), (hipStream_t)stream));
+                                                                   out->fmt, (hipStream_t)stream));
   return QLORA_OK;
 }
 
@@ -254,7 +254,7 @@ int qlora_quantize_nf4_dq_ws(const float* W, int64_t n, const qlora_nf4dq* out, 
   if ((st = device_status())) return st;
   hipStream_t hs = (hipStream_t)stream;
   QL_RUN(QLORA_K_QUANTIZE, hs, launch_quantize(W, n, out->codes, out->scale8, out->scale2, d_flags,
-                                               host_codebook(out->fmt), hs));
+                                               out->fmt, hs));
   QL_RUN(QLORA_K_QUANTIZE, hs, launch_dq_variant(W, n, out->scale8, out->scale2, out->dq,
                                                  static_cast<double*>(ws), hs));
   return QLORA_OK;

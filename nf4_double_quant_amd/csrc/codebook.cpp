@@ -17,6 +17,7 @@
 // bit, over 6; FP4 E3M0 = sign and 3 exponent bits, field 0 = zero, field e
 // = 2^(e−7).  Both FP4 tables keep −0 and +0.
 #include <cmath>
+#include <cstring>
 
 #include "common.h"
 
@@ -93,11 +94,47 @@ Codebook build_e3m0() {
   return build_signed(mag, 1.0);
 }
 
+// Number of midpoints strictly below x: the code of a weight with w/c1 = x.
+int code_below(const Codebook& cb, double x) {
+  int k = 0;
+  for (int t = 0; t < 15; ++t) k += cb.mid[t] < x;
+  return k;
+}
+
+EncodeGuide build_guide(const Codebook& cb) {
+  constexpr double S = kGuideScale;
+  uint8_t code[sizeof(EncodeGuide::packed)];
+  for (size_t c = 0; c < sizeof(code); ++c)
+    code[c] = (uint8_t)(c < (size_t)kGuideCells ? code_below(cb, ((double)c - S - 0.5) / S) : 15);
+  bool ok = true;
+  for (int c = 0; c + 1 < kGuideCells; ++c) ok = ok && code[c + 1] - code[c] <= 1;
+  ok = ok && code_below(cb, 1.0) - code[kGuideCells - 1] <= 1;   // the last cell, up to x = 1
+  for (int t = 0; t < 15; ++t) {
+    const double e = cb.mid[t] * S + S + 0.5;   // exact: S is a power of two
+    if (e > -1.0 && e < kGuideCells + 1.0) ok = ok && std::fabs(e - std::nearbyint(e)) > 1e-3;
+  }
+  EncodeGuide g;
+  std::memcpy(g.packed, code, sizeof(code));
+  g.zero_cell = -1;
+  for (int c = 0; c < kGuideCells && ok; ++c)
+    if (code[c] == 7) {
+      g.zero_cell = c;
+      break;
+    }
+  return g;
+}
+
 }  // namespace
 
 const Codebook& host_codebook(int fmt) {
   static const Codebook tables[4] = {build_nf4(), build_int4(), build_e2m1(), build_e3m0()};
   return tables[fmt >= 0 && fmt < 4 ? fmt : 0];
+}
+
+const EncodeGuide& host_encode_guide(int fmt) {
+  static const EncodeGuide guides[4] = {build_guide(host_codebook(0)), build_guide(host_codebook(1)),
+                                        build_guide(host_codebook(2)), build_guide(host_codebook(3))};
+  return guides[fmt >= 0 && fmt < 4 ? fmt : 0];
 }
 
 }  // namespace qlora

@@ -28,6 +28,22 @@ struct Codebook {
 // 1 = int4, 2 = FP4 E2M1, 3 = FP4 E3M0 (the qlora_fmt values).
 const Codebook& host_codebook(int fmt = 0);
 
+// First guess of the encode.  Cell c = floor(x·S + S + 1/2) of x = w/c1 in
+// [-1, 1] covers [(c − S − 1/2)/S, (c − S + 1/2)/S); code[c] is the number
+// of midpoints below the cell's lower edge.  The builder checks that every
+// cell holds at most one midpoint and that no midpoint lies within 1/1000 of
+// a cell of an edge; then for any cell computed from x with an error below
+// that margin, the code of w is code[c] or code[c] + 1, and one threshold
+// compare decides.  zero_cell is a cell whose code is 7 (all-zero blocks),
+// or −1 when the table fails the checks.
+constexpr int kGuideScale = 128;
+constexpr int kGuideCells = 2 * kGuideScale + 1;
+struct EncodeGuide {
+  uint32_t packed[(kGuideCells + 3) / 4];   // byte c = code[c]
+  int32_t zero_cell;
+};
+const EncodeGuide& host_encode_guide(int fmt = 0);
+
 __device__ __forceinline__ uint16_t bf16_bits(float x) {
   // gfx950 converts with round-to-nearest-even (v_cvt_pk_bf16_f32).
   __bf16 h = (__bf16)x;

@@ -7,9 +7,10 @@
 namespace qlora {
 
 
-// cb: the 16-entry table of the codes (host_codebook(fmt)).
+// fmt: the 16-entry table of the codes (host_codebook(fmt), with its
+// host_encode_guide(fmt)); hipErrorInvalidValue when the guide is unusable.
 hipError_t launch_quantize(const float* W, int64_t n, uint8_t* codes, uint8_t* scale8,
-                           float* scale2, int32_t* flags, const Codebook& cb, hipStream_t st);
+                           float* scale2, int32_t* flags, int fmt, hipStream_t st);
 // dq: second-level variant (0 default; 1 int8 around the tensor mean; 2 E4M3
 // around it, the mean stored after the steps in scale2).
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scale8, const float* scale2,

@@ -8,28 +8,35 @@
 // gfx950 design
 //  * One workgroup per double-quant group (16384 weights = 64 KB of fp32):
 //    the group's second-level constant needs every block's absmax, so the
-//    whole group stays in VGPRs (16 float4 per lane) between the reduction
-//    and the encode, and HBM is read exactly once.
-//  * 16 lanes per 64-weight block, one float4 each: every load instruction
-//    covers 1 KB contiguous.  The block absmax is a 16-lane xor-shuffle max
-//    on the integer bits of |w| (integer order equals float order for
-//    non-negative floats, and NaN/Inf land above every finite value, which
-//    is how non-finite input is detected).
-//  * Exact nearest-value encode without fp64 per weight: for each block the
-//    15 decision points c1·mid_t are exact fp64 products; rounding each one
-//    DOWN to fp32 gives a threshold th_t with  w > c1·mid_t  <=>  w > th_t
-//    for every fp32 w.  A thread per block builds them once, as unsigned
-//    keys with the order of the fp32 values, into shared memory; each weight
-//    then takes a 4-level binary search that reads one threshold per level
-//    and shifts the comparison's borrow into the code (two VALU operations).
-//  * Codes are packed 8 per 32-bit word (byte j = code j | code j+4 << 4):
-//    the two lanes holding a word's halves merge them with one shuffle, the
-//    words are gathered in LDS and written out as 16-byte stores.
+//    whole group is loaded at once into VGPRs (16 float4 per lane) and HBM
+//    is read exactly once.
+//  * 8 lanes per 64-weight block, 8 consecutive weights per lane.  A block
+//    is encoded and stored as soon as its two loads land: its codes need
+//    only its own absmax, so the encode overlaps the rest of the group's
+//    loads, and only the small second level waits for the whole group.
+//  * The block absmax is an 8-lane DPP max on the integer bits of |w|
+//    (integer order equals float order for non-negative floats, and NaN/Inf
+//    land above every finite value, which is how non-finite input is
+//    detected).
+//  * Exact nearest-value encode without fp64 per weight: the 15 decision
+//    points c1·mid_t are exact fp64 products; rounding each one DOWN to fp32
+//    gives a threshold th_t with  w > c1·mid_t  <=>  w > th_t  for every
+//    fp32 w.  The 8 lanes of a block compute its 16 entries (the last one
+//    +inf) into shared memory.  A weight's code is then a guess and one
+//    compare: the cell of w·S/c1 on a 1/S grid (S = 128) indexes a table of
+//    the code at each cell's lower edge, which the host built so that the
+//    true code is that code or the next one, and  w > th_guess  adds the 1.
+//    Blocks whose absmax is zero, non-finite or below 2^-100 take a rare,
+//    wave-uniform branch that keeps the cell index in range.
+//  * Each lane packs its 8 codes into one 32-bit word (byte j = code j |
+//    code j+4 << 4) and a wave's store covers 8 consecutive blocks (256 B).
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace qlora {
 
-// Largest fp32 <= the exact (nonzero) fp64 value p.
+// Largest fp32 <= the exact fp64 value p (NaN stays NaN).
 __device__ __forceinline__ float round_down_f32(double p) {
   float f = (float)p;
   if ((double)f > p) {
@@ -39,27 +46,12 @@ __device__ __forceinline__ float round_down_f32(double p) {
   return f;
 }
 
-// Unsigned key with the order of the fp32 values (-0 just below +0): for the
-// thresholds used here, none of them -0, k(w) > k(t) exactly when w > t.
-__device__ __forceinline__ uint32_t order_key(float x) {
-  const uint32_t b = __float_as_uint(x);
-  return b ^ ((uint32_t)((int32_t)b >> 31) | 0x80000000u);
-}
-
-// 2k + (t < u): the borrow of t - u carried into k + k (two VALU operations)
-__device__ __forceinline__ uint32_t bit_in(uint32_t k, uint32_t t, uint32_t u) {
-  uint32_t d, r;
-  asm("v_sub_co_u32 %0, vcc, %2, %3\n\tv_addc_co_u32 %1, vcc, %4, %4, vcc"
-      : "=&v"(d), "=v"(r) : "v"(t), "v"(u), "v"(k) : "vcc");
-  return r;
-}
-
-// max over the 16 lanes of a DPP row (rotations by 8, 4, 2, 1)
-__device__ __forceinline__ uint32_t row_max16(uint32_t a) {
-  a = max(a, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, 0x128, 0xF, 0xF, false));
-  a = max(a, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, 0x124, 0xF, 0xF, false));
-  a = max(a, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, 0x122, 0xF, 0xF, false));
-  a = max(a, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, 0x121, 0xF, 0xF, false));
+// max over the 8 lanes of each half of a DPP row (rotations by 4, 2, 1
+// within the half: row_half_mirror then quad permutes)
+__device__ __forceinline__ uint32_t row_max8(uint32_t a) {
+  a = max(a, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, 0x141, 0xF, 0xF, false));  // half-row mirror
+  a = max(a, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, 0x4E, 0xF, 0xF, false));   // quad [2,3,0,1]
+  a = max(a, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, 0xB1, 0xF, 0xF, false));   // quad [1,0,3,2]
   return a;
 }
 
@@ -77,35 +69,139 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, i
                                                   uint8_t* __restrict__ codes,
                                                   uint8_t* __restrict__ scale8,
                                                   float* __restrict__ scale2,
-                                                  int32_t* __restrict__ flags, Codebook cb) {
-  __shared__ __attribute__((aligned(16))) uint32_t s_thr[kGroup][16];   // threshold order keys
-  __shared__ __attribute__((aligned(16))) uint32_t s_codes[kGroupElems / 8];
+                                                  int32_t* __restrict__ flags, Codebook cb,
+                                                  EncodeGuide eg) {
+  __shared__ __attribute__((aligned(16))) float s_thr[kGroup][16];   // per-block thresholds
+  __shared__ uint32_t s_guide[(kGuideCells + 3) / 4];
+  __shared__ double s_mid[16];
   __shared__ uint32_t s_c1[kGroup];
   __shared__ uint32_t s_red[4];
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int sub = lane & 15, quad = lane >> 4;
+  const int sub = lane & 7, row = lane >> 3;      // 8 lanes per block, 8 weights per lane
   const int64_t g = blockIdx.x;
   const int64_t base = g * kGroupElems;
   const int64_t nb = (n + kBlock - 1) / kBlock;
+  const int64_t nvalid = n - base;
 
-  // ---- load the group (reads past n return 0) and take per-block absmax
-  const Rsrc rw = rsrc(W + base, (min((int64_t)kGroupElems, n - base)) * 4);
+  // ---- issue every load of the group (reads past n return 0)
+  const Rsrc rw = rsrc(W + base, (min((int64_t)kGroupElems, nvalid)) * 4);
   float4 v[16];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int bl = wave * 64 + j * 4 + quad;
-    const int off = (bl * kBlock + sub * 4) * 4;
-    v[j] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 0));
+  for (int j = 0; j < 8; ++j) {
+    const int bl = wave * 64 + j * 8 + row;
+    const int off = (bl * kBlock + sub * 8) * 4;
+    v[2 * j] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 0));
+    v[2 * j + 1] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rw, off + 16, 0, 0));
   }
-  uint32_t bad = 0;
+  if (t < (kGuideCells + 3) / 4) s_guide[t] = eg.packed[t];
+  if (t < 16) s_mid[t] = t < 15 ? cb.mid[t] : __builtin_inf();
+  __syncthreads();
+  // this lane's two thresholds of each block: indices sub and sub + 8
+  // (index 15 is +inf: a code never exceeds 15)
+  const double mid_lo = s_mid[sub], mid_hi = s_mid[sub + 8];
+  const uint8_t* guide = reinterpret_cast<const uint8_t*>(s_guide);
+  const float zero_base = (float)eg.zero_cell + 0.5f;
+  const float cell_base = (float)kGuideScale + 0.5f;
+
+  const int nv_group = (int)min(nvalid, (int64_t)kGroupElems);    // 32-bit: a scalar test
+  const bool ragged = nv_group < kGroupElems && (nv_group & 7) != 0;
+  const int64_t code_bytes = (n + 7) / 8 * 4;
+  const int64_t cbase = g * (kGroupElems / 2);
+  const Rsrc rcod = rsrc(codes + cbase, code_bytes - cbase);
+
+  // ---- pass 1, per block as its loads land: absmax, thresholds and the
+  // factors of the cell computation
+  uint32_t bad = 0, tiny_any = 0;
+  float inv[8];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    uint32_t a = max(max(abs_bits(v[j].x), abs_bits(v[j].y)), max(abs_bits(v[j].z), abs_bits(v[j].w)));
-    a = row_max16(a);
+  for (int j = 0; j < 8; ++j) {
+    const int bl = wave * 64 + j * 8 + row;
+    const float4 p = v[2 * j], q = v[2 * j + 1];
+    uint32_t a = max(max(max(abs_bits(p.x), abs_bits(p.y)), max(abs_bits(p.z), abs_bits(p.w))),
+                     max(max(abs_bits(q.x), abs_bits(q.y)), max(abs_bits(q.z), abs_bits(q.w))));
+    a = row_max8(a);
     bad |= (a >= 0x7F800000u);
-    if (sub == 0) s_c1[wave * 64 + j * 4 + quad] = a;
+    s_c1[bl] = a;                                  // the 8 lanes agree
+    const float c1 = __uint_as_float(a);
+    const double c1d = (double)c1;
+    // th_t = c1·mid_t rounded down to fp32: w > th_t exactly when w > c1·mid_t
+    s_thr[bl][sub] = round_down_f32(c1d * mid_lo);
+    s_thr[bl][sub + 8] = round_down_f32(c1d * mid_hi);
+    // S/c1 = 1/(c1·2^-7) with S = 128: for c1 in [2^-100, FLT_MAX] both the
+    // argument and the result of the reciprocal are normal floats.  Blocks
+    // with 0 < c1 < 2^-100 scale w and c1 by 2^64 (pass 2's generic copy);
+    // all-zero and non-finite blocks take zero_cell.
+    const bool normal = a - 0x0D800000u < 0x7F800000u - 0x0D800000u;
+    const bool tiny = a - 1u < 0x0D800000u - 1u;
+    tiny_any |= tiny;
+    inv[j] = normal ? __builtin_amdgcn_rcpf(c1 * 0x1p-7f)
+           : tiny   ? __builtin_amdgcn_rcpf(c1 * 0x1p57f)
+                    : 0.0f;                            // (a finite reciprocal is never 0)
   }
+
+  // ---- pass 2: encode and store.  The cell of x = w/c1 gives a guide code
+  // that is the code of w or one below it, and one threshold compare decides.
+  // Straight-line over the eight blocks unless a block is tiny or the group
+  // ends inside a code word.
+  auto encode_store = [&](auto generic) {
+    constexpr bool kGeneric = decltype(generic)::value;
+#pragma unroll
+    for (int jp = 0; jp < 8; jp += 2) {                // two blocks at a time
+      uint32_t cell[16], g0[16], k[16];
+      float th[16];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int j = jp + h;
+        const float4 p = v[2 * j], q = v[2 * j + 1];
+        const float w[8] = {p.x, p.y, p.z, p.w, q.x, q.y, q.z, q.w};
+        float sc = 1.0f;
+        if constexpr (kGeneric) sc = s_c1[wave * 64 + j * 8 + row] - 1u < 0x0D800000u - 1u ? 0x1p64f : 1.0f;
+        // inv = 0 marks an all-zero or non-finite block
+        const float c0 = inv[j] != 0.0f ? cell_base : zero_base;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = kGeneric ? w[e] * sc : w[e];
+          // v_cvt_u32_f32: NaN (a non-finite block) gives 0, still a valid cell
+          asm("v_cvt_u32_f32 %0, %1" : "=v"(cell[8 * h + e]) : "v"(__builtin_fmaf(x, inv[j], c0)));
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) g0[e] = guide[cell[e]];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) th[e] = s_thr[wave * 64 + (jp + (e >> 3)) * 8 + row][g0[e]];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int j = jp + h;
+        const float4 p = v[2 * j], q = v[2 * j + 1];
+        const float w[8] = {p.x, p.y, p.z, p.w, q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) k[8 * h + e] = g0[8 * h + e] + (w[e] > th[8 * h + e] ? 1u : 0u);
+        const uint32_t* kk = k + 8 * h;
+        // word `sub` of the block: byte e = code e | code e+4 << 4
+        uint32_t word = (kk[0] | (kk[4] << 4)) | ((kk[1] | (kk[5] << 4)) << 8) |
+                        ((kk[2] | (kk[6] << 4)) << 16) | ((kk[3] | (kk[7] << 4)) << 24);
+        const int wi = (wave * 64 + j * 8 + row) * 8 + sub;     // word within the group
+        if constexpr (kGeneric) {
+          // The word holding code n-1 may end in codes past n; they are
+          // stored as 7, the layout's padding, whatever a zero weight
+          // encodes to.
+          const int nv = nv_group - wi * 8;                     // valid codes of this word
+          if (nv > 0 && nv < 8) {
+            uint32_t keep = 0;
+            for (int c = 0; c < nv; ++c) keep |= 0xFu << (8 * (c & 3) + 4 * (c >> 2));
+            word = (word & keep) | (0x77777777u & ~keep);
+          }
+        }
+        // (stores past the code buffer are dropped)
+        __builtin_amdgcn_raw_buffer_store_b32(word, rcod, wi * 4, 0, 0);
+      }
+    }
+  };
+  if (ragged || __builtin_amdgcn_ballot_w64(tiny_any != 0))
+    encode_store(std::true_type{});
+  else
+    encode_store(std::false_type{});
   __syncthreads();
 
   // ---- second level: one thread per block
@@ -134,75 +230,6 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, i
   const int64_t b_glob = g * kGroup + t;
   if (b_glob < nb) scale8[b_glob] = (uint8_t)q;
   if (t == 0) scale2[g] = step;
-
-  // decision thresholds of this block
-  {
-    float th[16];
-    if (c1_bits == 0) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) th[i] = i < 7 ? -1.0f : 0.0f;  // everything -> code 7
-    } else {
-#pragma unroll
-      for (int i = 0; i < 15; ++i) th[i] = round_down_f32((double)c1 * cb.mid[i]);
-      th[15] = 0.0f;
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) s_thr[t][i] = order_key(th[i]);
-  }
-  __syncthreads();
-
-  // ---- encode
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int bl = wave * 64 + j * 4 + quad;
-    // binary search on order keys, level by level for the four weights:
-    // k collects the code bits from the top, and each level reads the one
-    // threshold it compares against (index 8k+3, 4k+1, 2k)
-    const uint32_t* T = s_thr[bl];
-    const uint32_t t7 = T[7];
-    const uint32_t u[4] = {order_key(v[j].x), order_key(v[j].y), order_key(v[j].z), order_key(v[j].w)};
-    uint32_t kk[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) kk[e] = bit_in(0u, t7, u[e]);
-#pragma unroll
-    for (int lev = 0; lev < 3; ++lev) {
-      uint32_t th[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) th[e] = T[lev == 0 ? 8 * kk[e] + 3 : lev == 1 ? 4 * kk[e] + 1 : 2 * kk[e]];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) kk[e] = bit_in(kk[e], th[e], u[e]);
-    }
-    const uint32_t k0 = kk[0], k1 = kk[1], k2 = kk[2], k3 = kk[3];
-    // lane `sub` holds codes 4·sub..4·sub+3 of the block: low nibbles of a
-    // word for even sub, high nibbles for odd sub; neighbours merge by DPP
-    const uint32_t half = (k0 | (k1 << 8) | (k2 << 16) | (k3 << 24)) << ((sub & 1) * 4);
-    const uint32_t other = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)half, 0xB1, 0xF, 0xF, false);
-    if ((sub & 1) == 0) s_codes[bl * 8 + (sub >> 1)] = half | other;
-  }
-  __syncthreads();
-
-  // ---- write the group's 8192 code bytes (stores past the buffer are dropped)
-  const int64_t code_bytes = (n + 7) / 8 * 4;
-  const int64_t cbase = g * (kGroupElems / 2);
-  const Rsrc rcod = rsrc(codes + cbase, code_bytes - cbase);
-  uint4 a = reinterpret_cast<const uint4*>(s_codes)[t * 2];
-  uint4 b = reinterpret_cast<const uint4*>(s_codes)[t * 2 + 1];
-  // The word holding code n-1 may end in codes past n; they are stored as 7,
-  // the layout's padding, whatever a zero weight encodes to in this table.
-  const int64_t nvalid = n - base;
-  if (nvalid < kGroupElems && (nvalid & 7) != 0 && (nvalid >> 6) == t) {
-    uint32_t keep = 0;
-    for (int j = 0; j < (int)(nvalid & 7); ++j) keep |= 0xFu << (8 * (j & 3) + 4 * (j >> 2));
-    const int wi = (int)((nvalid >> 3) & 7);
-    uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-      if (k == wi) w[k] = (w[k] & keep) | (0x77777777u & ~keep);
-    a = make_uint4(w[0], w[1], w[2], w[3]);
-    b = make_uint4(w[4], w[5], w[6], w[7]);
-  }
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) int, a), rcod, t * 32, 0, 0);
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) int, b), rcod, t * 32 + 16, 0, 0);
   if (bad && flags != nullptr) flags[0] = flags[0] | 1;
 }
 
@@ -388,11 +415,13 @@ hipError_t launch_dq_variant(const float* W, int64_t n, uint8_t* scale8, float* 
 
 // ------------------------------------------------------------------ launchers
 hipError_t launch_quantize(const float* W, int64_t n, uint8_t* codes, uint8_t* scale8,
-                           float* scale2, int32_t* flags, const Codebook& cb, hipStream_t st) {
+                           float* scale2, int32_t* flags, int fmt, hipStream_t st) {
   const int64_t ng = (n + kGroupElems - 1) / kGroupElems;
   if (ng == 0) return hipSuccess;
+  const EncodeGuide& eg = host_encode_guide(fmt);
+  if (eg.zero_cell < 0) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_quantize, dim3((unsigned)ng), dim3(256), 0, st, W, n, codes, scale8,
-                     scale2, flags, cb);
+                     scale2, flags, host_codebook(fmt), eg);
   return hipGetLastError();
 }
 

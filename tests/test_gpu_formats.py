@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 import synth
-from gpu_util import bf16_dev, bf16_host_f64, bf16_to_f64, check_close
+from gpu_util import bf16_dev, bf16_host_f64, bf16_to_f64, check_close, grid_and_scale_blocks
 from oracle import formats, linear, nf4
 
 pytestmark = pytest.mark.gpu
@@ -87,6 +87,11 @@ def test_ragged_exact(fmt, n):
 @pytest.mark.parametrize("fmt", OTHER)
 def test_ties_and_zeros_exact(fmt):
     assert_exact(_with_ties(fmt, 9), fmt, f"{fmt} ties")
+
+
+@pytest.mark.parametrize("fmt", OTHER)
+def test_grid_points_and_extreme_scales_exact(fmt):
+    assert_exact(grid_and_scale_blocks(formats.codebook(fmt), 33), fmt, f"{fmt} grid")
 
 
 @pytest.mark.parametrize("fmt", OTHER)

@@ -2,7 +2,8 @@
 
 Cases: the 128×128 workload, ragged lengths (partial blocks and groups),
 adversarial values (exact ties between codebook values and between scale
-levels, zero blocks and groups, subnormals, huge magnitudes), non-finite
+levels, zero blocks and groups, subnormals, huge magnitudes), weights on a
+fine grid of w/c1 and at the edges of the fp32 range, non-finite
 input, determinism, and the full-size weight shapes of the 4096×4096 layer,
 the 7B-style MLP (11008×4096) and the 65B-style MLP (22016×8192), the last
 two checked on sampled double-quant groups (quantization is group-local).
@@ -12,6 +13,7 @@ import numpy as np
 import pytest
 
 import synth
+from gpu_util import grid_and_scale_blocks
 from oracle import nf4
 
 pytestmark = pytest.mark.gpu
@@ -100,6 +102,16 @@ def _adversarial():
 def test_adversarial_values():
     w = _adversarial()
     q = assert_quant_exact(w, "adversarial")
+    ref = nf4.dequant_f32(*nf4.quantize(w), w.size)
+    got = qb.qlora_dequant(q, torch.float32).cpu().numpy().ravel()
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def test_grid_points_and_extreme_scales():
+    w = grid_and_scale_blocks(nf4.codebook(), 31)
+    w = np.concatenate([w, (np.random.default_rng(32).standard_normal(GE - w.size % GE) * 0.02)
+                        .astype(np.float32)])
+    q = assert_quant_exact(w, "grid and extreme scales")
     ref = nf4.dequant_f32(*nf4.quantize(w), w.size)
     got = qb.qlora_dequant(q, torch.float32).cpu().numpy().ravel()
     assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
