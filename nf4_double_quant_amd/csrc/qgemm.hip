@@ -23,8 +23,9 @@
 //  * forward: the weight tile is [n][k] like the activation tile (k-major
 //    rows, XOR-swizzled 16-byte chunks), read with ds_read_b128;
 //  * backward: a block is 64 consecutive n of one k, so the tile is stored
-//    [k][n] (16-byte chunks swizzled by 4·(k mod 4)) and the MFMA B operand
-//    is gathered with ds_read_b64_tr_b16, four k of one n per lane per read.
+//    [k][n] (16-byte chunks placed by chunk_tr) and
+//    the MFMA B operand is gathered with ds_read_b64_tr_b16, four k of one n
+//    per lane per read.
 // The adapter term is one (or a few) extra k-steps over [s·T ‖ B] or
 // [s·U ‖ A], accumulated into the same registers, so Y and dX are rounded
 // to bf16 once.  B [r][o] is n-major like the backward weight tile and A
@@ -52,6 +53,19 @@ constexpr int kWaves = 4;
 // rows, and rows 8 apart, land in different chunks.  It depends on row % 32
 // only.
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 3); }
+
+// Position of 16-byte chunk c (0..15) in row k of a [k][n] tile (256-byte
+// rows): c ^ h(k mod 4) with h = 0, 3, 6, 5, then bit 3 flipped by bit 1 of
+// c and by bit 2 of k (a bijection of the chunks of each row).  A transposed
+// fragment read covers 4 consecutive rows × 2 adjacent chunks per 16 lanes,
+// and the two 16-lane groups of a half-wave chunks 2 apart; an expansion
+// write covers rows k..k+3 (8 lanes) or k..k+7 (16 lanes) with 2 chunks 4
+// apart.  The positions differ mod 8 within 16 lanes of a read and 8 lanes
+// of a write, and mod 16 within 32 and 16 lanes, so neither conflicts with
+// 32 banks nor with 64.
+__device__ __forceinline__ int chunk_tr(int k, int c) {
+  return c ^ (((k & 3) << 1) ^ (k & 3)) ^ (((k >> 2) & 1) << 3) ^ ((c & 2) << 2);
+}
 
 __device__ __forceinline__ s16x4 lds_tr(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3)))*)(p));
@@ -240,7 +254,7 @@ __global__ __launch_bounds__(64 * kWaves) void k_qgemm(QGemmArgs p) {
     if (!kTransW) {
       return sb + wrow_n * kBK + (((kCW * pp + c) ^ swz(wrow_n)) << 3);
     } else {
-      return sb + wrow_k * kBN + (((8 * hb + kCW * pp + c) ^ ((wrow_k & 3) << 2)) << 3);
+      return sb + wrow_k * kBN + (chunk_tr(wrow_k, 8 * hb + kCW * pp + c) << 3);
     }
   };
 
@@ -275,14 +289,15 @@ __global__ __launch_bounds__(64 * kWaves) void k_qgemm(QGemmArgs p) {
       for (int j = 0; j < 4; ++j) f.b[j] = *reinterpret_cast<const bf16x8*>(pb + j * 32 * kBK);
     } else {
       const int g = lane >> 4, s = lane & 15;
-      const int kr = kk * 16 + 8 * (g >> 1) + (s >> 2);          // kr % 4 == s / 4
+      const int kr = kk * 16 + 8 * (g >> 1) + (s >> 2);
+      const uint16_t* qlo = sb + kr * kBN + 4 * (s & 1);
+      const uint16_t* qhi = qlo + 4 * kBN;                            // rows kr + 4
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        // logical 16-byte chunk 4j + 2(g%2) + (s%4)/2, swizzled by 4·(kr%4)
-        const int c = 4 * (j ^ (s >> 2)) + 2 * (g & 1) + ((s & 3) >> 1);
-        const uint16_t* q = sb + kr * kBN + (c << 3) + 4 * (s & 1);
-        const s16x4 lo = lds_tr(q);
-        const s16x4 hi = lds_tr(q + 4 * kBN);                       // rows kr+4: same swizzle
+        // logical 16-byte chunk 4j + 2(g%2) + (s%4)/2 of rows kr and kr + 4
+        const int c = 4 * j + 2 * (g & 1) + ((s & 3) >> 1);
+        const s16x4 lo = lds_tr(qlo + (chunk_tr(kr, c) << 3));
+        const s16x4 hi = lds_tr(qhi + (chunk_tr(kr + 4, c) << 3));
         const s16x8 bv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         f.b[j] = __builtin_bit_cast(bf16x8, bv);
       }
@@ -433,7 +448,7 @@ __global__ __launch_bounds__(64 * kWaves) void k_qgemm(QGemmArgs p) {
           *reinterpret_cast<uint4*>(sB0 + row * kBK + ((ch ^ swz(row)) << 3)) = rb[i];
         } else {
           const int kr = c >> 4, ch = c & 15;
-          *reinterpret_cast<uint4*>(sB0 + kr * kBN + ((ch ^ ((kr & 3) << 2)) << 3)) = rb[i];
+          *reinterpret_cast<uint4*>(sB0 + kr * kBN + (chunk_tr(kr, ch) << 3)) = rb[i];
         }
       }
       plain_step(ATag{});
