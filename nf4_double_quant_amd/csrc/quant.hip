@@ -36,14 +36,22 @@
 
 namespace qlora {
 
-// Largest fp32 <= the exact fp64 value p (NaN stays NaN).
-__device__ __forceinline__ float round_down_f32(double p) {
-  float f = (float)p;
-  if ((double)f > p) {
-    int32_t bits = __float_as_int(f);
-    f = __int_as_float(bits > 0 ? bits - 1 : bits + 1);  // toward −inf
-  }
-  return f;
+// The largest fp32 values <= two fp64 values: the conversions run with the
+// wave's fp32 rounding mode (MODE bits 1:0) set to toward −inf, restored to
+// nearest-even inside the same block so no other arithmetic sees it (the
+// block is then a pure function of its inputs and may be scheduled freely).
+__device__ __forceinline__ float2 round_down_pair(double a, double b) {
+  float x, y;
+  asm(
+      "s_setreg_imm32_b32 hwreg(HW_REG_MODE, 0, 2), 2\n\t"
+      "s_nop 1\n\t"
+      "v_cvt_f32_f64 %0, %2\n\t"
+      "v_cvt_f32_f64 %1, %3\n\t"
+      "s_setreg_imm32_b32 hwreg(HW_REG_MODE, 0, 2), 0\n\t"
+      "s_nop 1"
+      : "=&v"(x), "=&v"(y)
+      : "v"(a), "v"(b));
+  return make_float2(x, y);
 }
 
 // max over the 8 lanes of each half of a DPP row (rotations by 4, 2, 1
@@ -126,18 +134,17 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, i
     const float c1 = __uint_as_float(a);
     const double c1d = (double)c1;
     // th_t = c1·mid_t rounded down to fp32: w > th_t exactly when w > c1·mid_t
-    s_thr[bl][sub] = round_down_f32(c1d * mid_lo);
-    s_thr[bl][sub + 8] = round_down_f32(c1d * mid_hi);
+    const float2 th = round_down_pair(c1d * mid_lo, c1d * mid_hi);
+    s_thr[bl][sub] = th.x;
+    s_thr[bl][sub + 8] = th.y;
     // S/c1 = 1/(c1·2^-7) with S = 128: for c1 in [2^-100, FLT_MAX] both the
     // argument and the result of the reciprocal are normal floats.  Blocks
     // with 0 < c1 < 2^-100 scale w and c1 by 2^64 (pass 2's generic copy);
     // all-zero and non-finite blocks take zero_cell.
-    const bool normal = a - 0x0D800000u < 0x7F800000u - 0x0D800000u;
     const bool tiny = a - 1u < 0x0D800000u - 1u;
     tiny_any |= tiny;
-    inv[j] = normal ? __builtin_amdgcn_rcpf(c1 * 0x1p-7f)
-           : tiny   ? __builtin_amdgcn_rcpf(c1 * 0x1p57f)
-                    : 0.0f;                            // (a finite reciprocal is never 0)
+    const float rc = __builtin_amdgcn_rcpf(c1 * (a < 0x0D800000u ? 0x1p57f : 0x1p-7f));
+    inv[j] = a - 1u < 0x7F7FFFFFu ? rc : 0.0f;       // finite, nonzero c1 (a finite reciprocal is never 0)
   }
 
   // ---- pass 2: encode and store.  The cell of x = w/c1 gives a guide code
