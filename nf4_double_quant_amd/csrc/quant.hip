@@ -10,10 +10,12 @@
 //    the group's second-level constant needs every block's absmax, so the
 //    whole group is loaded at once into VGPRs (16 float4 per lane) and HBM
 //    is read exactly once.
-//  * 8 lanes per 64-weight block, 8 consecutive weights per lane.  A block
-//    is encoded and stored as soon as its two loads land: its codes need
-//    only its own absmax, so the encode overlaps the rest of the group's
-//    loads, and only the small second level waits for the whole group.
+//  * 8 lanes per 64-weight block, 8 consecutive weights per lane.  A
+//    block's codes need only its own absmax, so only the small second level
+//    waits for the whole group: pass 1 takes each block's absmax, thresholds
+//    and cell reciprocal as its two loads land; pass 2 encodes the eight
+//    blocks of a lane two at a time (their LDS reads in flight together)
+//    and stores them.
 //  * The block absmax is an 8-lane DPP max on the integer bits of |w|
 //    (integer order equals float order for non-negative floats, and NaN/Inf
 //    land above every finite value, which is how non-finite input is
@@ -26,8 +28,9 @@
 //    compare: the cell of w·S/c1 on a 1/S grid (S = 128) indexes a table of
 //    the code at each cell's lower edge, which the host built so that the
 //    true code is that code or the next one, and  w > th_guess  adds the 1.
-//    Blocks whose absmax is zero, non-finite or below 2^-100 take a rare,
-//    wave-uniform branch that keeps the cell index in range.
+//    All-zero and non-finite blocks take the cell of a code-7 guess;
+//    blocks with absmax below 2^-100 (and a group that ends inside a code
+//    word) take a rare, wave-uniform generic copy of pass 2.
 //  * Each lane packs its 8 codes into one 32-bit word (byte j = code j |
 //    code j+4 << 4) and a wave's store covers 8 consecutive blocks (256 B).
 #include <type_traits>
