@@ -96,7 +96,16 @@ def pmc_summary(fetch_csv: str, write_csv: str, workload: str) -> dict:
                         "k_qgemm_kib_per_dispatch": statistics.mean(main), "dispatches": len(main)}
     fetch = out["FETCH_SIZE"]["k_qgemm_kib_per_dispatch"] * 1024 * out["FETCH_SIZE"]["factor"]
     write = out["WRITE_SIZE"]["k_qgemm_kib_per_dispatch"] * 1024 * out["WRITE_SIZE"]["factor"]
+    commands = [
+        "rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_fetch -o fetch -- "
+        "python3 bench.py --pmc --steps 3",
+        "rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_write -o write -- "
+        "python3 bench.py --pmc --steps 3",
+        "python3 bench.py --pmc-summary " + os.path.relpath(fetch_csv, ROOT) + " "
+        + os.path.relpath(write_csv, ROOT),
+    ]
     return {"workload": workload, "kernel": "k_qgemm (forward and backward launches averaged)",
+            "commands": commands,
             "kernel_source_hash": kernel_source_hash(), "counters": out,
             "hbm_fetch_bytes_per_launch": round(fetch), "hbm_write_bytes_per_launch": round(write),
             "hbm_bytes_per_launch": round(fetch + write)}
