@@ -96,13 +96,13 @@ def pmc_summary(fetch_csv: str, write_csv: str, workload: str) -> dict:
                         "k_qgemm_kib_per_dispatch": statistics.mean(main), "dispatches": len(main)}
     fetch = out["FETCH_SIZE"]["k_qgemm_kib_per_dispatch"] * 1024 * out["FETCH_SIZE"]["factor"]
     write = out["WRITE_SIZE"]["k_qgemm_kib_per_dispatch"] * 1024 * out["WRITE_SIZE"]["factor"]
+    fetch_rel, write_rel = os.path.relpath(fetch_csv, ROOT), os.path.relpath(write_csv, ROOT)
     commands = [
-        "rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_fetch -o fetch -- "
+        f"rocprofv3 --pmc FETCH_SIZE -f csv -d {os.path.dirname(fetch_rel)} -o fetch -- "
         "python3 bench.py --pmc --steps 3",
-        "rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_write -o write -- "
+        f"rocprofv3 --pmc WRITE_SIZE -f csv -d {os.path.dirname(write_rel)} -o write -- "
         "python3 bench.py --pmc --steps 3",
-        "python3 bench.py --pmc-summary " + os.path.relpath(fetch_csv, ROOT) + " "
-        + os.path.relpath(write_csv, ROOT),
+        f"python3 bench.py --pmc-summary {fetch_rel} {write_rel}",
     ]
     return {"workload": workload, "kernel": "k_qgemm (forward and backward launches averaged)",
             "commands": commands,
@@ -126,7 +126,7 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(the layer would shard by tokens with an all-reduce of dA, dB; not built).",
               file=sys.stderr)
         sys.exit(2)
