@@ -193,6 +193,39 @@ def _need(t, dtype, name, device=None):
         raise ValueError(f"{name} is on {t.device}, expected {device}")
 
 
+def _tensor(t, name):
+    torch = _torch()
+    if t is not None and not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+
+
+def _shape(t, shape, name):
+    """ValueError unless tensor t (if given) has exactly `shape`.  Checked
+    before anything reaches the library: the C ABI receives sizes only, so a
+    mis-shaped buffer would otherwise be read or written past its end."""
+    if t is None:
+        return
+    _tensor(t, name)
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _numel(t, n, name):
+    if t is None:
+        return
+    _tensor(t, name)
+    if t.numel() != n:
+        raise ValueError(f"{name} holds {t.numel()} elements, expected {n}")
+
+
+def _linear_dims(q, name="q"):
+    shape = getattr(q, "shape", None)
+    if shape is None or len(shape) != 2 or int(shape[0]) * int(shape[1]) != q.n:
+        raise ValueError(f"{name} must be a quantized 2-D weight [o][d]")
+    q.check_buffers()
+    return int(shape[0]), int(shape[1])
+
+
 @dataclass
 class QuantizedWeight:
     """Device buffers of a quantized tensor: codes, 8-bit scales, fp32 steps."""
@@ -205,8 +238,23 @@ class QuantizedWeight:
     dq: int = 0
 
     def view(self) -> _NF4DQ:
+        self.check_buffers()
         return _NF4DQ(self.codes.data_ptr(), self.scale8.data_ptr(), self.scale2.data_ptr(), self.n,
                       self.fmt, self.dq)
+
+    def check_buffers(self):
+        """ValueError unless every buffer holds at least the bytes the layout
+        of n weights needs (4 bits per weight, one byte per 64, one fp32 per
+        16384, plus the mean for the centred second levels)."""
+        n = int(self.n)
+        nb = -(-n // QLORA_BLOCK)
+        need = {"codes": 4 * -(-n // 8), "scale8": nb,
+                "scale2": 4 * -(-nb // QLORA_GROUP) + (4 if self.dq and n > 0 else 0)}
+        for name, nbytes in need.items():
+            t = getattr(self, name)
+            have = t.numel() * t.element_size()
+            if have < nbytes:
+                raise ValueError(f"quantized {name} holds {have} bytes, {nbytes} needed for n={n}")
 
     @property
     def device(self):
@@ -234,6 +282,7 @@ def qlora_quantize_nf4_dq(W, check_finite: bool = True, out: QuantizedWeight | N
     """
     torch = _torch()
     _need(W, torch.float32, "W")
+    _tensor(W, "W")
     if out is not None and out.n != W.numel():
         raise ValueError("out holds a different number of weights")
     dq_code = DQ_VARIANTS[dq] if isinstance(dq, str) else int(dq)
@@ -294,7 +343,12 @@ def qlora_dequant(q: QuantizedWeight, dtype=None):
 
 
 class Workspace:
-    """Grow-only device scratch buffer reused across calls on one stream."""
+    """Grow-only device scratch buffer reused across calls on one stream.
+
+    Calls that share a Workspace must be ordered (one stream, or streams
+    synchronised by the caller): a later call may overwrite, or regrow and
+    free, the buffer while an earlier call's kernels still use it.  The
+    default workspaces are kept per (device, stream) for that reason."""
 
     def __init__(self, device=None):
         self.device = device
@@ -312,7 +366,9 @@ _default_ws: dict = {}
 
 def _workspace(ws, device, nbytes):
     if ws is None:
-        ws = _default_ws.setdefault(str(device), Workspace())
+        torch = _torch()
+        key = (str(device), torch.cuda.current_stream(device).cuda_stream)
+        ws = _default_ws.setdefault(key, Workspace())
     return ws.get(nbytes, device)
 
 
@@ -323,9 +379,19 @@ def qlora_linear_fwd(X, q: QuantizedWeight, A, B, s: float, want_T: bool = True,
     Returns (Y, T) with T = X·A in fp32 (None if want_T is False or r == 0).
     """
     torch = _torch()
-    M, d = X.shape
-    o = q.shape[0]
-    r = 0 if A is None else A.shape[1]
+    o, d = _linear_dims(q)
+    _tensor(X, "X")
+    if X.dim() != 2:
+        raise ValueError(f"X must be 2-D [M][d], got shape {tuple(X.shape)}")
+    M = X.shape[0]
+    _shape(X, (M, d), "X")
+    if (A is None) != (B is None):
+        raise ValueError("A and B are given together or not at all")
+    _tensor(A, "A")
+    r = 0 if A is None else (A.shape[1] if A.dim() == 2 else -1)
+    _shape(A, (d, r), "A")
+    _shape(B, (r, o), "B")
+    _shape(out, (M, o), "out")
     for t, nm in ((X, "X"), (A, "A"), (B, "B")):
         _need(t, torch.bfloat16, nm, X.device)
     Y = torch.empty((M, o), dtype=torch.bfloat16, device=X.device) if out is None else out
@@ -343,9 +409,20 @@ def qlora_linear_bwd(dY, X, T, q: QuantizedWeight, A, B, s: float, need_dX: bool
                      ws=None):
     """(dX, dA, dB) of the layer; no gradient for the 4-bit weight.  T may be None."""
     torch = _torch()
-    M, o = dY.shape
-    d = q.shape[1]
-    r = 0 if A is None else A.shape[1]
+    o, d = _linear_dims(q)
+    _tensor(dY, "dY")
+    if dY.dim() != 2:
+        raise ValueError(f"dY must be 2-D [M][o], got shape {tuple(dY.shape)}")
+    M = dY.shape[0]
+    _shape(dY, (M, o), "dY")
+    if (A is None) != (B is None):
+        raise ValueError("A and B are given together or not at all")
+    _tensor(A, "A")
+    r = 0 if A is None else (A.shape[1] if A.dim() == 2 else -1)
+    _shape(A, (d, r), "A")
+    _shape(B, (r, o), "B")
+    _shape(X, (M, d), "X")
+    _shape(T, (M, r), "T")
     for t, nm in ((dY, "dY"), (X, "X"), (A, "A"), (B, "B")):
         _need(t, torch.bfloat16, nm, dY.device)
     _need(T, torch.float32, "T", dY.device)
@@ -370,14 +447,23 @@ def qlora_linear_fwd_multi(X, q: QuantizedWeight, A, B, s, adapter, want_T: bool
     base alone.  Returns (Y, T) with T = X[m]·A[adapter[m]] in fp32 (or None).
     """
     torch = _torch()
-    M, d = X.shape
-    o = q.shape[0]
-    n, _, r = A.shape
+    o, d = _linear_dims(q)
+    _tensor(X, "X")
+    if X.dim() != 2:
+        raise ValueError(f"X must be 2-D [M][d], got shape {tuple(X.shape)}")
+    M = X.shape[0]
+    _shape(X, (M, d), "X")
+    _tensor(A, "A")
+    if A is None or B is None or A.dim() != 3:
+        raise ValueError("A must be [n][d][r] and B [n][r][o]")
+    n, r = A.shape[0], A.shape[2]
+    _shape(A, (n, d, r), "A")
+    _shape(B, (n, r, o), "B")
+    _shape(adapter, (M,), "adapter")
+    _shape(out, (M, o), "out")
     for t, nm in ((X, "X"), (A, "A"), (B, "B")):
         _need(t, torch.bfloat16, nm, X.device)
     _need(adapter, torch.int32, "adapter", X.device)
-    if adapter.numel() != M:
-        raise ValueError("adapter must hold one index per token")
     svals = [float(v) for v in s]
     if len(svals) != n:
         raise ValueError("s must hold one scale per adapter")
@@ -396,8 +482,14 @@ def qlora_linear_fwd_multi(X, q: QuantizedWeight, A, B, s, adapter, want_T: bool
 def qlora_merge_adapter(q: QuantizedWeight, A, B, s: float, out=None):
     """fp32 [o][d] merged weight ŵ + s·(A·B)ᵀ, ready for qlora_quantize_nf4_dq."""
     torch = _torch()
-    o, d = q.shape
-    r = 0 if A is None else A.shape[1]
+    o, d = _linear_dims(q)
+    if (A is None) != (B is None):
+        raise ValueError("A and B are given together or not at all")
+    _tensor(A, "A")
+    r = 0 if A is None else (A.shape[1] if A.dim() == 2 else -1)
+    _shape(A, (d, r), "A")
+    _shape(B, (r, o), "B")
+    _shape(out, (o, d), "out")
     for t, nm in ((A, "A"), (B, "B")):
         _need(t, torch.bfloat16, nm, q.device)
     W = torch.empty((o, d), dtype=torch.float32, device=q.device) if out is None else out
@@ -415,11 +507,16 @@ def qlora_adamw_step(p, p16, g, m, v, step, lr=1e-4, beta1=0.9, beta2=0.999, eps
                      weight_decay=0.0):
     """AdamW on device tensors: p, m, v fp32 (in place), g bf16, p16 bf16 or None."""
     torch = _torch()
+    _tensor(p, "p")
+    n = p.numel()
+    for t, nm in ((m, "m"), (v, "v"), (g, "g"), (p16, "p16")):
+        _numel(t, n, nm)
+    if m is None or v is None or g is None:
+        raise ValueError("m, v and g are required")
     _need(p, torch.float32, "p")
     for t, nm, dt in ((m, "m", torch.float32), (v, "v", torch.float32), (g, "g", torch.bfloat16),
                       (p16, "p16", torch.bfloat16)):
         _need(t, dt, nm, p.device)
-    n = p.numel()
     h = _adamw(step, lr, beta1, beta2, eps, weight_decay)
     _check(lib().qlora_adamw_step(_ptr(p), _ptr(p16), _ptr(g), _ptr(m), _ptr(v), n, ctypes.byref(h),
                                   _stream(p.device)), "qlora_adamw_step")
@@ -436,6 +533,11 @@ def qlora_paged_adamw_step(p, p16, g, m_host, v_host, step, pool, lr=1e-4, beta1
     """AdamW with the states in pinned host tensors, paged through `pool` (a
     device uint8 tensor of at least 4096 bytes)."""
     torch = _torch()
+    _tensor(p, "p")
+    for t, nm in ((g, "g"), (p16, "p16"), (m_host, "m_host"), (v_host, "v_host")):
+        _numel(t, p.numel(), nm)
+    if g is None or m_host is None or v_host is None or pool is None:
+        raise ValueError("g, m_host, v_host and pool are required")
     _need(p, torch.float32, "p")
     for t, nm, dt in ((g, "g", torch.bfloat16), (p16, "p16", torch.bfloat16),
                       (pool, "pool", torch.uint8)):

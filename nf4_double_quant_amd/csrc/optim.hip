@@ -130,7 +130,10 @@ constexpr int kSlots = 4;   // pool slots, each an m page and a v page
 
 // The copy streams (one per direction, so host-to-device and device-to-host
 // transfers overlap) and events of the paged step, one set per device,
-// created on first use and kept for the life of the process.
+// created on first use and kept for the life of the process.  One mutex
+// covers their creation and every call's whole enqueue, and each call's
+// copies wait for the previous call's write-back, so calls from several
+// threads or caller streams run one after another on the device.
 struct PagedRes {
   hipStream_t in = nullptr, out = nullptr;
   hipEvent_t loaded[kSlots] = {}, done[kSlots] = {}, freed[kSlots] = {};
@@ -144,8 +147,7 @@ hipError_t paged_res(PagedRes** out) {
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  std::lock_guard<std::mutex> lock(g_paged_mu);
-  PagedRes& r = g_paged[dev];
+  PagedRes& r = g_paged[dev];   // the caller holds g_paged_mu
   if (r.in == nullptr) {
     if ((e = hipStreamCreateWithFlags(&r.in, hipStreamNonBlocking)) != hipSuccess) return e;
     if ((e = hipStreamCreateWithFlags(&r.out, hipStreamNonBlocking)) != hipSuccess) return e;
@@ -176,6 +178,7 @@ hipError_t launch_paged_adamw(float* p, uint16_t* p16, const uint16_t* g, float*
   if (n == 0) return hipSuccess;
   const int64_t page = paged_adamw_page_elems(pool_bytes);
   if (page <= 0) return hipErrorInvalidValue;
+  std::lock_guard<std::mutex> lock(g_paged_mu);
   PagedRes* R = nullptr;
   hipError_t e = paged_res(&R);
   if (e != hipSuccess) return e;
@@ -194,9 +197,12 @@ hipError_t launch_paged_adamw(float* p, uint16_t* p16, const uint16_t* g, float*
     if ((r = hipMemcpyAsync(slot_v(s), v_host + i * page, bytes, hipMemcpyHostToDevice, R->in)) != hipSuccess) return r;
     return hipEventRecord(R->loaded[s], R->in);
   };
-  // the pool and the host pages may still be in use by earlier work
+  // the pool and the host pages may still be in use by earlier work on the
+  // caller's stream, and the pool slots by the previous call's write-back
+  // (its finish event; a never-recorded event is complete)
   QL_CK(hipEventRecord(R->start, st));
   QL_CK(hipStreamWaitEvent(R->in, R->start, 0));
+  QL_CK(hipStreamWaitEvent(R->in, R->finish, 0));
   QL_CK(hipStreamWaitEvent(R->out, R->start, 0));
   for (int64_t i = 0; i < pages && i < kSlots; ++i) QL_CK(load(i));
   for (int64_t i = 0; i < pages; ++i) {

@@ -156,12 +156,14 @@ def test_full_linear_4096_sampled():
     check_close(T.cpu().numpy()[rows], Xf[rows] @ Af, "T rows")
 
 
-@pytest.mark.parametrize("pname", ["gate", "down"])
-def test_block_65b_projection_sampled(pname):
-    """65B-style shapes at their full size (gate 22016×8192, down 8192×22016,
-    2048 tokens, rank 64): sampled token rows of Y, dX and T, sampled rows of
-    dA and columns of dB, against the oracle's full dequantized weight."""
-    wl = synth.WORKLOADS["block_65b"]
+@pytest.mark.parametrize("wname,pname", [("block_65b", "gate"), ("block_65b", "down"),
+                                         ("block_7b", "gate"), ("block_7b", "down")])
+def test_block_projection_sampled(wname, pname):
+    """Block shapes at their full size: 65B-style gate 22016×8192 and down
+    8192×22016 at 2048 tokens, 7B-style gate 11008×4096 and down 4096×11008
+    at 4096 tokens, rank 64: sampled token rows of Y, dX and T, sampled rows
+    of dA and columns of dB, against the oracle's full dequantized weight."""
+    wl = synth.WORKLOADS[wname]
     p = next(pp for pp in wl.projs if pp.name == pname)
     W, X, A, B, dY = synth.layer_inputs(wl, p)
     Y, T, dX, dA, dB = run_gpu(W, X, A, B, dY, wl.s)

@@ -1,7 +1,8 @@
 """GPU parity of the adapter merge and the re-quantization that follows.
 
 The merged fp32 weight W' = fl32(ŵ + fl32(s·Δ)), Δ = A·B summed in fp32 in
-increasing rank order, is compared bit for bit with oracle.merge, and so are
+increasing rank order, is compared bit for bit with oracle.merge, and with
+the exact fp64 ŵ + s·(A·B)ᵀ within the rounding bound of such a sum, and so are
 the codes and scales of quantizing it again (same fp32 input on both sides).
 Shapes cover partial 128 × 128 tiles, ranks across the 64-wide rank chunks,
 r = 0, and the full 4096 × 4096, r = 64 layer.
@@ -11,6 +12,7 @@ import numpy as np
 import pytest
 
 import synth
+from bounds import merge_bound
 from gpu_util import bf16_dev, bf16_to_f64
 from oracle import merge, nf4
 
@@ -41,6 +43,11 @@ def check(o, d, r, s, seed):
     g = got.cpu().numpy()
     assert np.array_equal(g.view(np.uint32), ref.view(np.uint32)), \
         f"o={o} d={d} r={r}: {np.count_nonzero(g != ref)} merged weights differ"
+    # the plain definition, independent of the order of the fp32 rank sum:
+    # the exact ŵ + s·(A·B)ᵀ within the rounding bound of any such order
+    bound, exact = merge_bound(w_hat, bf16_to_f64(A), bf16_to_f64(B), s, r)
+    far = np.abs(g.astype(np.float64) - exact) > bound
+    assert not far.any(), f"o={o} d={d} r={r}: {int(far.sum())} merged weights outside the bound"
     rc, rs8, rs2 = nf4.quantize_chunked(ref.ravel())
     n_c, n_s8, n_s2 = qb.qlora_quant_sizes(o * d)
     assert np.array_equal(q2.codes.cpu().numpy()[:n_c], rc)

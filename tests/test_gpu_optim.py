@@ -1,12 +1,14 @@
 """GPU parity of the AdamW step of the adapter parameters, device-resident and
 paged from host memory, against oracle.adamw bit for bit (fp32 p, m, v and the
 bf16 copy of p), over consecutive steps, ragged lengths and pools small enough
-to force many pages."""
+to force many pages; and against the textbook fp64 AdamW update within the
+rounding bounds of an fp32 evaluation, independent of the operation order."""
 
 import numpy as np
 import pytest
 
 import synth
+from bounds import adamw_magnitudes, adamw_param_bound, adamw_state_bounds
 from oracle import adamw, nf4
 
 pytestmark = pytest.mark.gpu
@@ -92,3 +94,36 @@ def test_paged_step_bit_exact(n, pool_bytes):
                                   weight_decay=HP["weight_decay"])
         torch.cuda.synchronize()
         assert_same(f"paged n={n} pool={pool_bytes} t={t}", p, m, v, p16, ref[t - 1])
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_steps_within_bounds_of_fp64_definition(paged):
+    n = 4096 * 64 + 37
+    p0, _ = inputs(n, seed=11)
+    gl = grads(n, 11, 5)
+    p = torch.from_numpy(p0.copy()).cuda()
+    p16 = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    if paged:
+        m, v = qb.pinned_state(n), qb.pinned_state(n)
+        pool = torch.empty(256 << 10, dtype=torch.uint8, device="cuda")
+    else:
+        m, v = torch.zeros(n, device="cuda"), torch.zeros(n, device="cuda")
+    p64, m64, v64 = p0.astype(np.float64), np.zeros(n), np.zeros(n)
+    Mabs, Vabs = np.zeros(n), np.zeros(n)
+    for t in range(1, 6):
+        g = nf4.bf16_bits_to_f64(gl[t - 1])
+        kw = dict(lr=HP["lr"], beta1=HP["beta1"], beta2=HP["beta2"], eps=HP["eps"],
+                  weight_decay=HP["weight_decay"])
+        if paged:
+            qb.qlora_paged_adamw_step(p, p16, dev_bf16(gl[t - 1]), m, v, t, pool, **kw)
+        else:
+            qb.qlora_adamw_step(p, p16, dev_bf16(gl[t - 1]), m, v, t, **kw)
+        torch.cuda.synchronize()
+        p64, m64, v64 = adamw.step_fp64(p64, g, m64, v64, t, lr=HP["lr"], b1=HP["beta1"],
+                                        b2=HP["beta2"], eps=HP["eps"], wd=HP["weight_decay"])
+        gp, gm, gv = (x.cpu().numpy() for x in (p, m, v))
+        Mabs, Vabs = adamw_magnitudes(Mabs, Vabs, g, HP["beta1"], HP["beta2"])
+        bm, bv = adamw_state_bounds(t, Mabs, Vabs)
+        assert np.all(np.abs(gm - m64) <= bm), f"t={t}: m outside the bound"
+        assert np.all(np.abs(gv - v64) <= bv), f"t={t}: v outside the bound"
+        assert np.max(np.abs(gp - p64)) < adamw_param_bound(t), f"t={t}: p outside the bound"

@@ -5,6 +5,7 @@ pure decoupled decay; the bias corrections are the fp64 formula's."""
 
 import numpy as np
 
+from bounds import adamw_magnitudes, adamw_param_bound, adamw_state_bounds
 from oracle import adamw, nf4
 
 
@@ -24,17 +25,18 @@ def _state(n=4096, seed=1):
 def test_matches_textbook_fp64_over_several_steps():
     p, g, m, v = _state()
     p64, m64, v64 = p.astype(np.float64), m.astype(np.float64), v.astype(np.float64)
+    Mabs, Vabs = np.abs(m64), v64.copy()
     for t in range(1, 6):
-        mag_m = 0.9 * np.abs(m) + 0.1 * np.abs(g)       # size of the terms, for the bound
-        mag_v = 0.999 * np.abs(v) + 0.001 * g.astype(np.float64) ** 2
         p, m, v, _ = adamw.step(p, g, m, v, t, lr=2e-4, wd=0.01)
         p64, m64, v64 = adamw.step_fp64(p64, g, m64, v64, t, lr=2e-4, wd=0.01)
-        u = 2.0 ** -24
-        # the states carry fp32 rounding from each step: a few u per step of the term sizes
-        assert np.all(np.abs(m - m64) <= 4 * t * u * (mag_m + np.abs(m64)) + 1e-30)
-        assert np.all(np.abs(v - v64) <= 4 * t * u * (mag_v + np.abs(v64)) + 1e-30)
+        # the states carry fp32 rounding from each step: a few u per step of
+        # the magnitudes the moments accumulate
+        Mabs, Vabs = adamw_magnitudes(Mabs, Vabs, g)
+        bm, bv = adamw_state_bounds(t, Mabs, Vabs)
+        assert np.all(np.abs(m - m64) <= bm)
+        assert np.all(np.abs(v - v64) <= bv)
         # p (|p| < 0.1) is rounded to fp32 once or twice per step
-        assert np.max(np.abs(p - p64)) < 3 * t * float(np.spacing(np.float32(0.1)))
+        assert np.max(np.abs(p - p64)) < adamw_param_bound(t)
 
 
 def test_first_step_from_zero_state_is_lr_times_sign():
@@ -70,3 +72,16 @@ def test_bias_corrections():
     assert np.isclose(lr1, np.float32(1e-3) / (1 - b1 ** 3), rtol=1e-7)
     assert np.isclose(rs, 1 / np.sqrt(1 - b2 ** 3), rtol=1e-7)
     assert keep == 1.0 and c1 == np.float32(1 - b1)
+
+
+def test_state_bound_catches_a_wrong_update():
+    """The state bound is tight enough that a wrong coefficient or a dropped
+    term of the update breaks it."""
+    p, g, m, v = _state(seed=5)
+    Mabs, Vabs = adamw_magnitudes(np.abs(m.astype(np.float64)), v.astype(np.float64), g)
+    bm, bv = adamw_state_bounds(1, Mabs, Vabs)
+    _, m64, v64 = adamw.step_fp64(p.astype(np.float64), g, m.astype(np.float64), v.astype(np.float64), 1)
+    _, m_bad, v_bad, _ = adamw.step(p, g, m, v, 1, b1=0.91)          # wrong beta1
+    assert np.any(np.abs(m_bad - m64) > bm)
+    _, m_ok, v_bad, _ = adamw.step(p, g, m, np.zeros_like(v), 1)     # v's carried term dropped
+    assert np.any(np.abs(v_bad - v64) > bv)

@@ -12,6 +12,7 @@ from fractions import Fraction
 import numpy as np
 
 import synth
+from bounds import merge_bound
 from oracle import merge, nf4
 
 
@@ -30,14 +31,8 @@ def _case(o=24, d=64, r=8, seed=3):
     return w_hat, A, B
 
 
-U = 2.0 ** -24          # unit roundoff of fp32
-
-
 def _bound(w_hat, A, B, s, r):
-    """|fl(merge) - exact| <= |s|·(r+1)·u·Σ_j|A B| + u·|ŵ + sΔ| (+ u² terms)."""
-    absum = np.abs(A) @ np.abs(B)                     # [d][o]
-    exact = w_hat.astype(np.float64) + s * (A @ B).T
-    return abs(s) * (r + 1) * U * absum.T * 1.0001 + U * np.abs(exact) * 1.0001, exact
+    return merge_bound(w_hat, A, B, s, r)
 
 
 def test_exact_rational_on_small_inputs():
