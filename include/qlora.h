@@ -65,6 +65,7 @@ extern "C" {
 #define QLORA_MAX_WEIGHTS (1LL << 31)   /* largest o*d of a linear layer      */
 #define QLORA_MAX_MULTI_TOKENS 16       /* largest M of qlora_linear_fwd_multi */
 #define QLORA_MAX_ADAPTERS 64           /* largest adapter count of the same   */
+#define QLORA_NOALLOC_SCRATCH_BYTES (64LL << 20)  /* static scratch of qlora_linear_bwd_noalloc */
 
 typedef enum {
   QLORA_OK = 0,
@@ -76,7 +77,9 @@ typedef enum {
   QLORA_E_WORKSPACE = 4,  /* ws_bytes below qlora_workspace_bytes()          */
   QLORA_E_NO_DEVICE = 5,  /* no HIP device visible to the process            */
   QLORA_E_HIP = 6,        /* a HIP launch or runtime call failed             */
-  QLORA_E_NONFINITE = 7   /* reserved for bindings: a flag word had bit 0 set */
+  QLORA_E_NONFINITE = 7,  /* reserved for bindings: a flag word had bit 0 set */
+  QLORA_E_SCRATCH = 8     /* the sizes need more scratch than the static buffer
+                             of qlora_linear_bwd_noalloc holds               */
 } qlora_status;
 
 typedef enum { QLORA_F32 = 0, QLORA_BF16 = 1 } qlora_dtype;
@@ -319,6 +322,25 @@ int qlora_linear_bwd(const qlora_bf16* dY, const qlora_bf16* X, const float* T,
                      const qlora_bf16* A, const qlora_bf16* B, int64_t r, float s,
                      qlora_bf16* dX, qlora_bf16* dA, qlora_bf16* dB,
                      void* ws, size_t ws_bytes, void* stream);
+
+/* qlora_linear_bwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, results (bitwise) and errors as qlora_linear_bwd, without
+ * ws and ws_bytes: the scratch is a static device array of the library,
+ * QLORA_NOALLOC_SCRATCH_BYTES (64 MiB) on each GPU it runs on, held from the
+ * first call on that GPU until the process ends.  Sizes whose
+ * qlora_workspace_bytes(QLORA_OP_BWD, M, d, o, r) exceeds it return
+ * QLORA_E_SCRATCH before any launch (at r = 64 every projection of a
+ * 7B-style block at 4096 tokens and of a 65B-style block at 2048 tokens fits:
+ * at most 60.5 MiB).  No call
+ * allocates or frees memory.  Every call on one GPU shares that GPU's array
+ * and leaves its contents behind (each call overwrites the scratch it
+ * reads): calls that overlap on one GPU (several streams or threads without
+ * ordering between them) race and give undefined results. */
+int qlora_linear_bwd_noalloc(const qlora_bf16* dY, const qlora_bf16* X, const float* T,
+                             int64_t M, int64_t d, const qlora_nf4dq* W, int64_t o,
+                             const qlora_bf16* A, const qlora_bf16* B, int64_t r, float s,
+                             qlora_bf16* dX, qlora_bf16* dA, qlora_bf16* dB, void* stream);
 
 /* ------------------------------------------------------------ diagnostics */
 

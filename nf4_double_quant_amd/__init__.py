@@ -8,7 +8,7 @@ built, or a tensor is not on a HIP device, the calls raise.
 Functions carry the C names:
   qlora_quant_sizes, qlora_codebook, qlora_workspace_bytes,
   qlora_quantize_nf4_dq, qlora_dequant, qlora_linear_fwd, qlora_linear_bwd,
-  qlora_linear_fwd_multi, qlora_merge_adapter, qlora_adamw_step,
+  qlora_linear_bwd_noalloc, qlora_linear_fwd_multi, qlora_merge_adapter, qlora_adamw_step,
   qlora_paged_adamw_step.
 """
 
@@ -21,7 +21,8 @@ from dataclasses import dataclass
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libqlora.so")
 
-QLORA_OK, QLORA_E_NONFINITE = 0, 7
+QLORA_OK, QLORA_E_NONFINITE, QLORA_E_SCRATCH = 0, 7, 8
+QLORA_NOALLOC_SCRATCH_BYTES = 64 << 20
 QLORA_F32, QLORA_BF16 = 0, 1
 QLORA_OP_FWD, QLORA_OP_BWD = 0, 1
 QLORA_BLOCK, QLORA_GROUP = 64, 256     # weights per block, blocks per double-quant group
@@ -75,6 +76,8 @@ def lib() -> ctypes.CDLL:
                                    vp, vp, vp, sz, vp]
     L.qlora_linear_bwd.argtypes = [vp, vp, vp, i64, i64, P(_NF4DQ), i64, vp, vp, i64,
                                    ctypes.c_float, vp, vp, vp, vp, sz, vp]
+    L.qlora_linear_bwd_noalloc.argtypes = [vp, vp, vp, i64, i64, P(_NF4DQ), i64, vp, vp, i64,
+                                           ctypes.c_float, vp, vp, vp, vp]
     L.qlora_adamw_step.argtypes = [vp, vp, vp, vp, vp, i64, P(_AdamW), vp]
     L.qlora_paged_adamw_step.argtypes = [vp, vp, vp, vp, vp, i64, P(_AdamW), vp, sz, vp]
     L.qlora_merge_adapter.argtypes = [P(_NF4DQ), i64, i64, vp, vp, i64, ctypes.c_float, vp, vp]
@@ -84,7 +87,8 @@ def lib() -> ctypes.CDLL:
     L.qlora_timing_read.argtypes = [i32, P(ctypes.c_double), P(i64)]
     for name in ("qlora_quant_sizes", "qlora_quant_sizes_dq", "qlora_quantize_nf4_dq_ws",
                  "qlora_codebook", "qlora_quantize_nf4_dq", "qlora_dequant",
-                 "qlora_linear_fwd", "qlora_linear_bwd", "qlora_linear_fwd_multi",
+                 "qlora_linear_fwd", "qlora_linear_bwd", "qlora_linear_bwd_noalloc",
+                 "qlora_linear_fwd_multi",
                  "qlora_merge_adapter", "qlora_adamw_step", "qlora_paged_adamw_step",
                  "qlora_timing_begin", "qlora_timing_end",
                  "qlora_timing_read"):
@@ -435,6 +439,41 @@ def qlora_linear_bwd(dY, X, T, q: QuantizedWeight, A, B, s: float, need_dX: bool
     _check(lib().qlora_linear_bwd(_ptr(dY), _ptr(X), _ptr(T), M, d, ctypes.byref(q.view()), o,
                                   _ptr(A), _ptr(B), r, float(s), _ptr(dX), _ptr(dA), _ptr(dB),
                                   _ptr(buf), buf.numel(), _stream(dev)), "qlora_linear_bwd")
+    return dX, dA, dB
+
+
+def qlora_linear_bwd_noalloc(dY, X, T, q: QuantizedWeight, A, B, s: float, dX, dA, dB):
+    """qlora_linear_bwd into caller-given outputs (dX may be None; dA, dB
+    None only with r == 0), with the library's static device scratch instead
+    of a workspace: nothing is allocated, in this function or the library.
+    Calls that overlap on one GPU race on that scratch."""
+    o, d = _linear_dims(q)
+    _tensor(dY, "dY")
+    if dY.dim() != 2:
+        raise ValueError(f"dY must be 2-D [M][o], got shape {tuple(dY.shape)}")
+    M = dY.shape[0]
+    _shape(dY, (M, o), "dY")
+    if (A is None) != (B is None):
+        raise ValueError("A and B are given together or not at all")
+    _tensor(A, "A")
+    r = 0 if A is None else (A.shape[1] if A.dim() == 2 else -1)
+    _shape(A, (d, r), "A")
+    _shape(B, (r, o), "B")
+    _shape(X, (M, d), "X")
+    _shape(T, (M, r), "T")
+    _shape(dX, (M, d), "dX")
+    _shape(dA, (d, r), "dA")
+    _shape(dB, (r, o), "dB")
+    if r > 0 and (dA is None or dB is None):
+        raise ValueError("dA and dB are required when r > 0")
+    torch = _torch()
+    dev = dY.device
+    for t, nm in ((dY, "dY"), (X, "X"), (A, "A"), (B, "B"), (dX, "dX"), (dA, "dA"), (dB, "dB")):
+        _need(t, torch.bfloat16, nm, dev)
+    _need(T, torch.float32, "T", dev)
+    _check(lib().qlora_linear_bwd_noalloc(_ptr(dY), _ptr(X), _ptr(T), M, d, ctypes.byref(q.view()), o,
+                                          _ptr(A), _ptr(B), r, float(s), _ptr(dX), _ptr(dA),
+                                          _ptr(dB), _stream(dev)), "qlora_linear_bwd_noalloc")
     return dX, dA, dB
 
 

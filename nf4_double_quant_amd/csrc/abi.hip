@@ -2,6 +2,7 @@
 // workspace layout and the launch sequence of each operation.
 #include <string.h>
 
+#include <mutex>
 #include <utility>
 #include <vector>
 
@@ -143,6 +144,31 @@ int check_linear_shapes(int64_t M, int64_t d, int64_t o, int64_t r, const qlora_
   return QLORA_OK;
 }
 
+// Scratch of qlora_linear_bwd_noalloc: a static device array, one copy per
+// GPU.  In host code `scratch` names a host-side stand-in, not the device
+// array; its device address comes from hipGetSymbolAddress, taken once per
+// device with that device current, and only that address is handed to
+// kernels.
+static __device__ __align__(256) uint8_t scratch[QLORA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+int scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return QLORA_E_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return QLORA_E_NO_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return QLORA_E_HIP;
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return QLORA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -179,6 +205,7 @@ const char* qlora_strerror(int status) {
     case QLORA_E_NO_DEVICE: return "no HIP device available";
     case QLORA_E_HIP: return "HIP runtime or launch failure";
     case QLORA_E_NONFINITE: return "non-finite weight in quantizer input";
+    case QLORA_E_SCRATCH: return "sizes need more scratch than the 64 MiB static buffer of qlora_linear_bwd_noalloc";
     default: return "unknown status";
   }
 }
@@ -457,6 +484,20 @@ int qlora_linear_bwd(const qlora_bf16* dY, const qlora_bf16* X, const float* T, 
                         lora ? r : 0, dX, d, host_codebook(W->fmt), hs));
   }
   return QLORA_OK;
+}
+
+int qlora_linear_bwd_noalloc(const qlora_bf16* dY, const qlora_bf16* X, const float* T, int64_t M,
+                             int64_t d, const qlora_nf4dq* W, int64_t o, const qlora_bf16* A,
+                             const qlora_bf16* B, int64_t r, float s, qlora_bf16* dX,
+                             qlora_bf16* dA, qlora_bf16* dB, void* stream) {
+  int st = check_linear_shapes(M, d, o, r, W);
+  if (st) return st;
+  if ((int64_t)bwd_layout(M, d, o, r).total > QLORA_NOALLOC_SCRATCH_BYTES) return QLORA_E_SCRATCH;
+  if ((st = device_status())) return st;
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws))) return st;
+  return qlora_linear_bwd(dY, X, T, M, d, W, o, A, B, r, s, dX, dA, dB, ws,
+                          (size_t)QLORA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 }  // extern "C"

@@ -87,7 +87,7 @@ def test_workspace_and_strings(L):
             qb.qlora_workspace_bytes(op, M, d, o, r)
     assert qb.qlora_workspace_bytes(qb.QLORA_OP_FWD, 1, 64, 8, 512) == 0
     assert "gfx950" in L.qlora_version().decode()
-    for st in range(8):
+    for st in range(9):
         assert qb.strerror(st)
 
 
@@ -213,6 +213,28 @@ def test_no_device_status(L):
                               A16, 1 << 30, None) == 5
     # size-0 work is a no-op even without a device
     assert L.qlora_quantize_nf4_dq(A16, 0, ctypes.byref(_view(0)), None, None) == 0
+    # the allocation-free backward: sizes that fit reach the device probe
+    assert L.qlora_linear_bwd_noalloc(A16, A16, None, 8, 128, ctypes.byref(v), 128, A16, A16, 8,
+                                      2.0, A16, A16, A16, None) == 5
+
+
+def test_noalloc_backward_size_limit(L):
+    """Sizes whose backward workspace exceeds the 64 MiB static scratch get
+    QLORA_E_SCRATCH before any device access; the largest block shapes fit."""
+    limit = qb.QLORA_NOALLOC_SCRATCH_BYTES
+    f = L.qlora_linear_bwd_noalloc
+
+    def call(M, d, o, r=64):
+        v = _view(o * d)
+        return f(A16, A16, None, M, d, ctypes.byref(v), o, A16, A16, r, 2.0, A16, A16, A16, None)
+
+    for M, d, o in ((4096, 11008, 11008), (4096, 8192, 8192), (16384, 4096, 4096)):
+        assert qb.qlora_workspace_bytes(qb.QLORA_OP_BWD, M, d, o, 64) > limit
+        assert call(M, d, o) == 8
+    for M, d, o in ((4096, 4096, 4096), (4096, 4096, 11008), (4096, 11008, 4096),
+                    (2048, 8192, 22016), (2048, 22016, 8192)):
+        assert qb.qlora_workspace_bytes(qb.QLORA_OP_BWD, M, d, o, 64) <= limit
+    assert call(8, 100, 128) == 2                           # shape errors come first
 
 
 def test_stack_rows_layout_and_checks():
