@@ -131,9 +131,10 @@ constexpr int kSlots = 4;   // pool slots, each an m page and a v page
 // The copy streams (one per direction, so host-to-device and device-to-host
 // transfers overlap) and events of the paged step, one set per device,
 // created on first use and kept for the life of the process.  One mutex
-// covers their creation and every call's whole enqueue, and each call's
-// copies wait for the previous call's write-back, so calls from several
-// threads or caller streams run one after another on the device.
+// covers their creation and every call's whole enqueue, and a call's first
+// pages wait for the previous call's write-back of the same pool slot, so
+// calls from several threads or caller streams never overwrite a slot in
+// use (when they pass the same pool).
 struct PagedRes {
   hipStream_t in = nullptr, out = nullptr;
   hipEvent_t loaded[kSlots] = {}, done[kSlots] = {}, freed[kSlots] = {};
@@ -192,17 +193,18 @@ hipError_t launch_paged_adamw(float* p, uint16_t* p16, const uint16_t* g, float*
     const int s = (int)(i % kSlots);
     const size_t bytes = (size_t)count(i) * sizeof(float);
     hipError_t r;
-    if (i >= kSlots && (r = hipStreamWaitEvent(R->in, R->freed[s], 0)) != hipSuccess) return r;
+    // the slot's last write-back: this call's page i - kSlots, or for the
+    // first pages the previous call's (an event never recorded is complete)
+    if ((r = hipStreamWaitEvent(R->in, R->freed[s], 0)) != hipSuccess) return r;
     if ((r = hipMemcpyAsync(slot_m(s), m_host + i * page, bytes, hipMemcpyHostToDevice, R->in)) != hipSuccess) return r;
     if ((r = hipMemcpyAsync(slot_v(s), v_host + i * page, bytes, hipMemcpyHostToDevice, R->in)) != hipSuccess) return r;
     return hipEventRecord(R->loaded[s], R->in);
   };
   // the pool and the host pages may still be in use by earlier work on the
-  // caller's stream, and the pool slots by the previous call's write-back
-  // (its finish event; a never-recorded event is complete)
+  // caller's stream (the slots' use by the previous call is covered by
+  // waiting for each slot's last write-back)
   QL_CK(hipEventRecord(R->start, st));
   QL_CK(hipStreamWaitEvent(R->in, R->start, 0));
-  QL_CK(hipStreamWaitEvent(R->in, R->finish, 0));
   QL_CK(hipStreamWaitEvent(R->out, R->start, 0));
   for (int64_t i = 0; i < pages && i < kSlots; ++i) QL_CK(load(i));
   for (int64_t i = 0; i < pages; ++i) {

@@ -263,3 +263,23 @@ def test_stacked_projections_match_separate_calls(M):
     torch.cuda.synchronize()
     # +0 terms of the block-diagonal B leave every sum unchanged (up to the sign of zero)
     assert torch.equal(Y[:, :o1].float(), Y1.float()) and torch.equal(Y[:, o1:].float(), Y2.float())
+
+
+def test_few_token_calls_on_one_workspace_are_deterministic():
+    """Repeated few-token calls on one workspace, shapes in turn, with and
+    without a T request, give the same bits every time."""
+    ws = qb.Workspace()
+    cases = []
+    for M, d, o, r, seed in ((1, 4096, 1040, 16, 71), (16, 11008, 264, 16, 72), (4, 640, 776, 72, 73)):
+        W, X, A, B, _ = make_case(M, d, o, r, seed)
+        q = qb.qlora_quantize_nf4_dq(torch.from_numpy(W).cuda())
+        cases.append((q, bf16_dev(X), bf16_dev(A), bf16_dev(B)))
+    first = []
+    for rep in range(8):
+        for i, (q, X, A, B) in enumerate(cases):
+            Y, T = qb.qlora_linear_fwd(X, q, A, B, 2.0, want_T=(rep % 2 == 0), ws=ws)
+            if rep == 0:
+                first.append(Y.clone())
+            elif not torch.equal(Y.view(torch.int16), first[i].view(torch.int16)):
+                raise AssertionError(f"case {i} differs at repetition {rep}")
+    torch.cuda.synchronize()
