@@ -33,9 +33,22 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
-PROFILE_PMC = os.path.join(ROOT, "profiles", "pmc_main_gemm_linear_4096.json")
-# the sources that define k_qgemm's code (kernels.h only declares launchers)
-KERNEL_SOURCES = ["qgemm.hip", "common.h"]
+PMC_FILE = os.path.join(ROOT, "profiles", "pmc_hbm_bytes.json")
+MFMA_FILE = os.path.join(ROOT, "profiles", "pmc_mfma_busy_k_qgemm_linear_4096.json")
+MFMA_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES", "GRBM_GUI_ACTIVE",
+                 "SQ_INSTS_VALU_MFMA_MOPS_BF16"]
+# Kernels whose HBM bytes per dispatch the counter passes record: name in the
+# trace, the sources that define its code, the workload it ran on, and the
+# grid size that selects its dispatches of that workload (None: all).
+PMC_KERNELS = {
+    "k_qgemm": ("k_qgemm", ["qgemm.hip", "common.h"], "linear_4096", None),
+    "k_quantize": ("k_quantize", ["quant.hip", "common.h"], "linear_4096", 1024 * 256),
+    "k_rank_down": ("k_rank_down", ["rank.hip", "common.h"], "linear_4096", None),
+    "k_rank_grad": ("k_rank_grad", ["rank.hip", "common.h"], "linear_4096", None),
+    "k_reduce_planes": ("k_reduce_planes", ["gemm.hip", "common.h"], "linear_4096", None),
+    "k_gemv<1>": ("k_gemv<1>", ["gemv.hip", "common.h"], "decode_mlp_7b", None),
+    "k_lora_down_small": ("k_lora_down_small", ["gemv.hip", "common.h"], "decode_mlp_7b", None),
+}
 
 
 def parse():
@@ -56,22 +69,41 @@ def parse():
     ap.add_argument("--pmc", action="store_true",
                     help="short run for hardware-counter passes: a 256 MiB device copy "
                          "(calibration of FETCH_SIZE/WRITE_SIZE) and --steps steps, no timing")
+    ap.add_argument("--mfma-summary", metavar="CSV",
+                    help="turn the counter_collection.csv of an MFMA-busy pass of --pmc into "
+                         + os.path.relpath(MFMA_FILE, ROOT))
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn the counter_collection.csv files of a FETCH_SIZE pass and a "
-                         "WRITE_SIZE pass of --pmc into " + os.path.relpath(PROFILE_PMC, ROOT))
+                         "WRITE_SIZE pass of --pmc into " + os.path.relpath(PMC_FILE, ROOT))
     return ap.parse_args()
 
 
-def kernel_source_hash() -> str:
+def source_hash(files) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in files:
         with open(os.path.join(ROOT, "nf4_double_quant_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def pmc_summary(fetch_csv: str, write_csv: str, workload: str) -> dict:
-    """HBM bytes per k_qgemm launch from a FETCH_SIZE and a WRITE_SIZE pass.
+def pmc_entry(kernel: str, workload: str):
+    """The kept counter figures of one kernel, or None when they are missing
+    or were taken on other sources or another workload."""
+    if not os.path.exists(PMC_FILE):
+        return None
+    with open(PMC_FILE) as f:
+        kept = json.load(f)
+    e = kept.get("kernels", {}).get(kernel)
+    if e is None or e.get("workload") != workload:
+        return None
+    if e.get("source_hash") != source_hash(PMC_KERNELS[kernel][1]):
+        return None
+    return e
+
+
+def pmc_summary(fetch_csv: str, write_csv: str) -> dict:
+    """HBM bytes per dispatch of each kernel in PMC_KERNELS from a FETCH_SIZE
+    pass and a WRITE_SIZE pass of `bench.py --pmc`.
 
     Each counter (KiB per dispatch) is scaled by the ratio of the known bytes
     of the calibration kernel (256 MiB read, 256 MiB written) to what the same
@@ -83,19 +115,30 @@ def pmc_summary(fetch_csv: str, write_csv: str, workload: str) -> dict:
         with open(path) as f:
             return [r for r in csv.DictReader(f) if r["Counter_Name"] == counter]
 
-    out = {}
+    factors, per = {}, {}
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         rs = rows(path, counter)
         cal = [float(r["Counter_Value"]) for r in rs if "MulFunctor" in r["Kernel_Name"]]
-        main = [float(r["Counter_Value"]) for r in rs if "k_qgemm" in r["Kernel_Name"]]
-        if not cal or not main:
-            raise SystemExit(f"{path}: no calibration or k_qgemm dispatches for {counter}")
+        if not cal:
+            raise SystemExit(f"{path}: no calibration dispatches for {counter}")
         cal_kib = statistics.median(cal)
-        factor = (256 << 20) / (cal_kib * 1024.0)
-        out[counter] = {"calibration_kib": cal_kib, "factor": factor,
-                        "k_qgemm_kib_per_dispatch": statistics.mean(main), "dispatches": len(main)}
-    fetch = out["FETCH_SIZE"]["k_qgemm_kib_per_dispatch"] * 1024 * out["FETCH_SIZE"]["factor"]
-    write = out["WRITE_SIZE"]["k_qgemm_kib_per_dispatch"] * 1024 * out["WRITE_SIZE"]["factor"]
+        factors[counter] = {"calibration_kib": cal_kib, "factor": (256 << 20) / (cal_kib * 1024.0)}
+        for name, (pat, _, _, grid) in PMC_KERNELS.items():
+            vals = [float(r["Counter_Value"]) for r in rs if pat in r["Kernel_Name"]
+                    and (grid is None or int(r["Grid_Size"]) == grid)]
+            if vals:
+                per.setdefault(name, {})[counter] = (statistics.mean(vals), len(vals))
+    kernels = {}
+    for name, c in per.items():
+        if "FETCH_SIZE" not in c or "WRITE_SIZE" not in c:
+            continue
+        fetch = c["FETCH_SIZE"][0] * 1024 * factors["FETCH_SIZE"]["factor"]
+        write = c["WRITE_SIZE"][0] * 1024 * factors["WRITE_SIZE"]["factor"]
+        kernels[name] = {"workload": PMC_KERNELS[name][2], "source_hash": source_hash(PMC_KERNELS[name][1]),
+                         "dispatches": c["FETCH_SIZE"][1],
+                         "hbm_fetch_bytes_per_dispatch": round(fetch),
+                         "hbm_write_bytes_per_dispatch": round(write),
+                         "hbm_bytes_per_dispatch": round(fetch + write)}
     fetch_rel, write_rel = os.path.relpath(fetch_csv, ROOT), os.path.relpath(write_csv, ROOT)
     commands = [
         f"rocprofv3 --pmc FETCH_SIZE -f csv -d {os.path.dirname(fetch_rel)} -o fetch -- "
@@ -104,11 +147,33 @@ def pmc_summary(fetch_csv: str, write_csv: str, workload: str) -> dict:
         "python3 bench.py --pmc --steps 3",
         f"python3 bench.py --pmc-summary {fetch_rel} {write_rel}",
     ]
-    return {"workload": workload, "kernel": "k_qgemm (forward and backward launches averaged)",
-            "commands": commands,
-            "kernel_source_hash": kernel_source_hash(), "counters": out,
-            "hbm_fetch_bytes_per_launch": round(fetch), "hbm_write_bytes_per_launch": round(write),
-            "hbm_bytes_per_launch": round(fetch + write)}
+    return {"commands": commands, "calibration": factors, "kernels": kernels}
+
+
+def mfma_summary(csv_path: str) -> dict:
+    """MFMA-busy figures of k_qgemm (forward and backward averaged) from one
+    counter pass of `bench.py --pmc` collecting MFMA_COUNTERS."""
+    import csv
+    with open(csv_path) as f:
+        rs = [r for r in csv.DictReader(f) if "k_qgemm" in r["Kernel_Name"]]
+    vals = {}
+    for c in MFMA_COUNTERS:
+        v = [float(r["Counter_Value"]) for r in rs if r["Counter_Name"] == c]
+        if v:
+            vals[c] = statistics.mean(v)
+    rel = os.path.relpath(csv_path, ROOT)
+    out = {"kernel": "k_qgemm (forward and backward launches averaged)", "workload": "linear_4096",
+           "source_hash": source_hash(PMC_KERNELS["k_qgemm"][1]), "counters_per_dispatch": vals,
+           "command": f"rocprofv3 --pmc {' '.join(MFMA_COUNTERS)} -f csv -d {os.path.dirname(rel)} "
+                      "-o mfma -- python3 bench.py --pmc --steps 3"}
+    # share of the CUs' busy cycles in which their matrix pipes were busy: the
+    # MFMA counter sums over the 4 SIMDs of each CU, the busy counter over CUs
+    if vals.get("SQ_BUSY_CU_CYCLES"):
+        out["mfma_busy_frac"] = round(vals["SQ_VALU_MFMA_BUSY_CYCLES"] / (4 * vals["SQ_BUSY_CU_CYCLES"]), 4)
+    if vals.get("SQ_INSTS_VALU_MFMA_MOPS_BF16"):
+        # bf16 MFMA work in units of 512 flop: checks the algorithmic count
+        out["mfma_flop_per_dispatch"] = vals["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
+    return out
 
 
 def step_flops(M, d, o, r):
@@ -117,9 +182,16 @@ def step_flops(M, d, o, r):
 
 def main():
     args = parse()
+    if args.mfma_summary:
+        res = mfma_summary(args.mfma_summary)
+        with open(MFMA_FILE, "w") as f:
+            json.dump(res, f, indent=1)
+            f.write("\n")
+        print(json.dumps(res))
+        return
     if args.pmc_summary:
-        res = pmc_summary(*args.pmc_summary, workload=args.workload)
-        with open(PROFILE_PMC, "w") as f:
+        res = pmc_summary(*args.pmc_summary)
+        with open(PMC_FILE, "w") as f:
             json.dump(res, f, indent=1)
             f.write("\n")
         print(json.dumps(res))
@@ -167,6 +239,15 @@ def main():
         for _ in range(args.steps):
             step()
         torch.cuda.synchronize()
+        # one pass of the 1-token decode over every weight set
+        dwl, sets, adapters, _ = decode_setup(args, qb, torch, np, synth, dev)
+        xs, ys = decode_inputs(qb, torch, np, synth, dev, dwl, 1)
+        dws = qb.Workspace()
+        for layer in sets:
+            for p_, qw in layer:
+                A_, B_ = adapters[p_.name]
+                qb.qlora_linear_fwd(xs[p_.name], qw, A_, B_, dwl.s, want_T=False, ws=dws, out=ys[p_.name])
+        torch.cuda.synchronize()
         print(json.dumps({"pmc_run": True, "copy_bytes": 256 << 20, "steps": args.steps}))
         return
 
@@ -176,8 +257,6 @@ def main():
 
     stream = torch.cuda.current_stream(dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    # inside the timed region only the dominant kernel carries launch events
-    qb.qlora_timing_begin([qb.K_MAIN_GEMM])
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e0.record(stream)
@@ -186,10 +265,8 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    qb.qlora_timing_end()
     ms_step_eager = e0.elapsed_time(e1) / args.steps
     wall_ms_step = (t1 - t0) * 1e3 / args.steps
-    gemm_ms, gemm_n = qb.qlora_timing_read(qb.K_MAIN_GEMM)
 
     # The same step captured once as a HIP graph and replayed: identical
     # kernels, no host launch gaps.  Its outputs are checked bitwise against
@@ -225,14 +302,13 @@ def main():
     except Exception as e:  # capture unsupported: the eager figure stands
         print(f"step graph capture failed: {e}", file=sys.stderr)
 
-    # per-class breakdown from a separate, fully instrumented pass
-    nb = max(5, args.steps // 5)
-    qb.qlora_timing_begin()
-    for _ in range(nb):
-        step()
-    torch.cuda.synchronize()
-    qb.qlora_timing_end()
-    per_class = {name: qb.qlora_timing_read(k) for name, k in qb.KERNEL_CLASSES.items()}
+    # Kernel time per class from one instrumented eager pass of `steps` steps
+    # (start/stop events recorded at the dispatches' own begin and end), after
+    # a warm-up pass that fills the library's event pool: the breakdown and
+    # the dominant kernel's launch time below both come from this pass.
+    per_class = instrumented_pass(qb, torch, step, args.steps)
+    gemm_ms, gemm_n = per_class["main_gemm"]
+    nb = args.steps
 
     flops = step_flops(M, d, o, r)
     value = flops / (ms_step * 1e-3) / 1e12
@@ -241,17 +317,18 @@ def main():
     gemm_flop_per_launch = (2 * M * d * o + 2 * M * r * o + 2 * M * o * d + 2 * M * r * d) / 2
     gemm_avg_ms = gemm_ms / max(gemm_n, 1)
     achieved = gemm_flop_per_launch / (gemm_avg_ms * 1e-3) / 1e12
-    traffic = None
-    if os.path.exists(PROFILE_PMC):
-        with open(PROFILE_PMC) as f:
-            pmc = json.load(f)
-        if pmc.get("kernel_source_hash") == kernel_source_hash() and pmc.get("workload") == wl.name:
-            traffic = pmc.get("hbm_bytes_per_launch")
+    kept = pmc_entry("k_qgemm", wl.name)
+    traffic = None if kept is None else kept["hbm_bytes_per_dispatch"]
     roofline = {"bound": "mfma", "kernel": "k_qgemm fused NF4 dequant-GEMM 512x128 (Y = X·Ŵ + sT·B, dX = dY·Ŵᵀ + sU·Aᵀ)",
                 "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                 "flop_per_launch": gemm_flop_per_launch, "avg_launch_us": round(gemm_avg_ms * 1e3, 2),
-                "launches": gemm_n}
+                "launches": gemm_n, "timing": "kernel begin/end events of the instrumented pass"}
+    if os.path.exists(MFMA_FILE):
+        with open(MFMA_FILE) as f:
+            mf = json.load(f)
+        if mf.get("source_hash") == source_hash(PMC_KERNELS["k_qgemm"][1]):
+            roofline["mfma_busy_frac"] = mf.get("mfma_busy_frac")
 
     breakdown = {name: {"ms_per_step": round(ms / nb, 4), "launches_per_step": n / nb}
                  for name, (ms, n) in per_class.items() if n}
@@ -286,19 +363,31 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+def instrumented_pass(qb, torch, fn, reps):
+    """{class name: (summed kernel ms, calls)} over `reps` calls of fn, every
+    kernel class timed at its dispatches (a warm-up pass fills the pool of
+    launch events first, so the measured pass creates none)."""
+    qb.qlora_timing_begin()
+    fn()
+    torch.cuda.synchronize()
+    qb.qlora_timing_begin()
+    for _ in range(reps):
+        fn()
+    torch.cuda.synchronize()
+    qb.qlora_timing_end()
+    return {name: qb.qlora_timing_read(k) for name, k in qb.KERNEL_CLASSES.items()}
+
+
 def _time_decode(qb, torch, sets, one, ys, byts, K_GEMV):
     """Time one MLP pass over every weight set: eager, then as a HIP-graph replay."""
     for layer in sets:
         one(layer)
     torch.cuda.synchronize()
     reps = max(2, 96 // len(sets))
-    # per-launch kernel time of the dequant-GEMV (eager, HIP events on the stream)
-    qb.qlora_timing_begin([K_GEMV])
-    for layer in sets:
-        one(layer)
-    torch.cuda.synchronize()
-    qb.qlora_timing_end()
-    gemv_ms, gemv_n = qb.qlora_timing_read(K_GEMV)
+    # kernel time per launch of the dequant-GEMV and of the T planes before it
+    cls = instrumented_pass(qb, torch, lambda: [one(layer) for layer in sets], 1)
+    gemv_ms, gemv_n = cls["gemv"]
+    tdown_ms, tdown_n = cls["adapter"]
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     # eager: one Python call per projection (host launch cost included)
     e0.record()
@@ -337,12 +426,15 @@ def _time_decode(qb, torch, sets, one, ys, byts, K_GEMV):
             "bytes_per_mlp": byts,
             "GBps": round(byts / (t * 1e-6) / 1e9, 1),
             "frac_of_hbm": round(byts / (t * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
-            "gemv_kernel_us": round(gemv_ms * 1e3 / max(gemv_n, 1), 2) if gemv_n else None}
+            "gemv_kernel_us": round(gemv_ms * 1e3 / max(gemv_n, 1), 2) if gemv_n else None,
+            "gemv_launches_per_mlp": gemv_n / len(sets),
+            "t_planes_kernel_us": round(tdown_ms * 1e3 / max(tdown_n, 1), 2) if tdown_n else None}
 
 
-def bench_decode(args, qb, torch, np, synth, dev):
-    """Few-token forward on 7B-style gate/up/down NF4 weights, rank 16, cycling
-    independent weight sets so the 256 MB MALL cannot hold them."""
+def decode_setup(args, qb, torch, np, synth, dev):
+    """(workload, weight sets, adapters, bf16 upload helper) of the decode
+    measurement: args.decode_sets independent sets of quantized gate, up and
+    down weights."""
     wl = synth.WORKLOADS["decode_mlp_7b"]
     # weight set 0 is the seeded host recipe; the other sets (only there to
     # defeat caching) come from a seeded device generator
@@ -367,13 +459,33 @@ def bench_decode(args, qb, torch, np, synth, dev):
     adapters = {p.name: (bfd(synth.normal_bf16((p.d, wl.r), 0.02, [wl.wid, synth.PROJ_IDS[p.name], synth.T_A])),
                          bfd(synth.normal_bf16((wl.r, p.o), 0.02, [wl.wid, synth.PROJ_IDS[p.name], synth.T_B])))
                 for p in wl.projs}
+    return wl, sets, adapters, bfd
+
+
+def decode_inputs(qb, torch, np, synth, dev, wl, M):
+    xs = {p.name: torch.from_numpy(synth.normal_bf16((M, p.d), 1.0, [wl.wid, synth.PROJ_IDS[p.name],
+                                                                     synth.T_X]).view(np.int16))
+          .view(torch.bfloat16).to(dev) for p in wl.projs}
+    ys = {p.name: torch.empty((M, p.o), dtype=torch.bfloat16, device=dev) for p in wl.projs}
+    return xs, ys
+
+
+def gemv_launch_bytes(qb, p, M, r):
+    """Algorithmic bytes one few-token dequant-GEMV launch moves: the 4-bit
+    codes, 8-bit scales and fp32 steps of the weight, X, B and Y (the T
+    planes it sums are a few KB and not counted)."""
+    c, s8, s2 = qb.qlora_quant_sizes(p.o * p.d)
+    return c + s8 + s2 + 2 * (M * p.d + r * p.o + M * p.o)
+
+
+def bench_decode(args, qb, torch, np, synth, dev):
+    """Few-token forward on 7B-style gate/up/down NF4 weights, rank 16, cycling
+    independent weight sets so the 256 MB MALL cannot hold them."""
+    wl, sets, adapters, bfd = decode_setup(args, qb, torch, np, synth, dev)
     res = {}
     ws = qb.Workspace()
     for M in (1, 4, 16):
-        xs = {p.name: torch.from_numpy(synth.normal_bf16((M, p.d), 1.0, [wl.wid, synth.PROJ_IDS[p.name],
-                                                                         synth.T_X]).view(np.int16))
-              .view(torch.bfloat16).to(dev) for p in wl.projs}
-        ys = {p.name: torch.empty((M, p.o), dtype=torch.bfloat16, device=dev) for p in wl.projs}
+        xs, ys = decode_inputs(qb, torch, np, synth, dev, wl, M)
         byts = 0
         for p in wl.projs:
             c, s8, s2 = qb.qlora_quant_sizes(p.o * p.d)
@@ -385,6 +497,8 @@ def bench_decode(args, qb, torch, np, synth, dev):
                 qb.qlora_linear_fwd(xs[p.name], qw, A, B, wl.s, want_T=False, ws=ws, out=ys[p.name])
 
         res[f"M{M}"] = _time_decode(qb, torch, sets, one, ys, byts, K_GEMV=qb.K_GEMV)
+        if M == 1:
+            roofline = decode_roofline(qb, wl, res["M1"])
 
     # gate and up read the same input in an MLP: run them as one projection of
     # 22016 rows with the two adapters side by side (A = [A_gate | A_up], B
@@ -448,7 +562,24 @@ def bench_decode(args, qb, torch, np, synth, dev):
                         "M*_gate_up_fused: gate and up share their input and run as one 22016-row "
                         "projection (adapters side by side, B block-diagonal); "
                         "M16_16_adapters: one adapter per token (16 adapters per projection)",
-            "weight_sets_cycled": len(sets), "peak_GBps": PEAK_HBM_GBPS, **res}
+            "weight_sets_cycled": len(sets), "peak_GBps": PEAK_HBM_GBPS, "roofline": roofline, **res}
+
+
+def decode_roofline(qb, wl, m1):
+    """HBM roofline of the few-token dequant-GEMV at 1 token: algorithmic
+    bytes per launch (averaged over gate, up and down) over its average
+    kernel time from the instrumented pass; traffic from the kept counters."""
+    per_launch = sum(gemv_launch_bytes(qb, p, 1, wl.r) for p in wl.projs) / len(wl.projs)
+    us = m1["gemv_kernel_us"]
+    achieved = per_launch / (us * 1e-6) / 1e9
+    traffic = pmc_entry("k_gemv<1>", wl.name)
+    tplanes = pmc_entry("k_lora_down_small", wl.name)
+    return {"bound": "hbm", "kernel": "k_gemv<1> fused NF4 dequant-GEMV, 1 token (gate, up, down)",
+            "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBPS, 4),
+            "traffic": None if traffic is None else traffic["hbm_bytes_per_dispatch"],
+            "bytes_per_launch": round(per_launch), "avg_launch_us": us,
+            "t_planes_traffic": None if tplanes is None else tplanes["hbm_bytes_per_dispatch"]}
 
 
 def bench_blocks(qb, torch, synth, dev, steps=5, warmup=2):

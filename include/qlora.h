@@ -355,13 +355,18 @@ typedef enum {
   QLORA_K_COUNT = 6
 } qlora_kernel_class;
 
-/* Launch timing for benchmarks: between qlora_timing_begin(mask) and
- * qlora_timing_end(), every launch of a class whose bit (1 << class) is set
- * in `mask` records a pair of HIP events on its own stream around the
- * kernel(s).  qlora_timing_read() waits for those events and returns the
- * summed elapsed milliseconds and the number of launches of one class.
- * Process-wide, not thread-safe; meant for single-threaded benchmark
- * drivers. */
+/* Launch timing for benchmarks (diagnostics only).  Between
+ * qlora_timing_begin(mask) and qlora_timing_end(), every call whose kernel
+ * class bit (1 << class) is set in `mask` launches its kernel(s) with a pair
+ * of HIP events recorded at the first dispatch's begin and the last
+ * dispatch's end (hipExtLaunchKernel), so the interval is kernel time, not
+ * host or queue time.  qlora_timing_read() waits for the events and returns
+ * the summed milliseconds and the number of calls of one class since the
+ * last qlora_timing_begin().  Events come from a pool that grows only when a
+ * pass needs more than any earlier pass did (run a warm-up pass first to
+ * keep event creation out of a timed pass).  The state is process-wide and
+ * not thread-safe: meant for single-threaded benchmark drivers; calls made
+ * while timing is off launch plainly and touch none of it. */
 int qlora_timing_begin(uint32_t mask);
 int qlora_timing_end(void);
 int qlora_timing_read(int kernel_class, double* total_ms, int64_t* launches);

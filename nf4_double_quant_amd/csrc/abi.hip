@@ -71,41 +71,59 @@ int device_status() {
   return cached;
 }
 
-// Event pairs recorded around launches while timing is on (diagnostics only).
+// Launch timing (diagnostics only; process-wide state, not thread-safe: one
+// benchmark driver thread).  While on, every call of a chosen kernel class
+// arms one start/stop event pair from a pool, and launch() records the
+// events at the dispatches' own begin and end.  The pool grows only when a
+// pass needs more pairs than any earlier one, so a warm-up pass leaves the
+// timed pass without event creation.
 struct LaunchTimer {
   bool on = false;
   uint32_t mask = 0;
-  std::vector<std::pair<hipEvent_t, hipEvent_t>> ev[QLORA_K_COUNT];
-  void clear() {
-    for (auto& v : ev) {
-      for (auto& p : v) {
-        (void)hipEventDestroy(p.first);    // diagnostics: nothing to do on failure
-        (void)hipEventDestroy(p.second);
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> pool;
+  size_t cursor = 0;
+  std::vector<size_t> used[QLORA_K_COUNT];
+  hipError_t next(size_t* idx) {
+    if (cursor == pool.size()) {
+      hipEvent_t a, b;
+      hipError_t e = hipEventCreate(&a);
+      if (e != hipSuccess) return e;
+      if ((e = hipEventCreate(&b)) != hipSuccess) {
+        (void)hipEventDestroy(a);   // diagnostics: nothing more to do on failure
+        return e;
       }
-      v.clear();
+      pool.push_back({a, b});
     }
+    *idx = cursor++;
+    return hipSuccess;
   }
 };
 LaunchTimer g_timer;
 
+}  // namespace
+
+namespace qlora {
+LaunchEvents*& armed_launch_events() {
+  static thread_local LaunchEvents* armed = nullptr;
+  return armed;
+}
+}  // namespace qlora
+
+namespace {
+
 template <class F>
 hipError_t timed(int cls, hipStream_t st, F&& f) {
+  (void)st;
   if (!g_timer.on || !((g_timer.mask >> cls) & 1u)) return f();
-  hipEvent_t a, b;
-  hipError_t e = hipEventCreate(&a);
+  size_t idx = 0;
+  hipError_t e = g_timer.next(&idx);
   if (e != hipSuccess) return e;
-  if ((e = hipEventCreate(&b)) != hipSuccess) {
-    (void)hipEventDestroy(a);
-    return e;
-  }
-  if ((e = hipEventRecord(a, st)) == hipSuccess && (e = f()) == hipSuccess) e = hipEventRecord(b, st);
-  if (e != hipSuccess) {
-    (void)hipEventDestroy(a);
-    (void)hipEventDestroy(b);
-    return e;
-  }
-  g_timer.ev[cls].push_back({a, b});
-  return hipSuccess;
+  LaunchEvents ev{g_timer.pool[idx].first, g_timer.pool[idx].second, false};
+  armed_launch_events() = &ev;
+  e = f();
+  armed_launch_events() = nullptr;
+  if (e == hipSuccess && ev.fired) g_timer.used[cls].push_back(idx);
+  return e;
 }
 
 #define QL_TRY(expr)                                  \
@@ -213,7 +231,8 @@ const char* qlora_strerror(int status) {
 const char* qlora_version(void) { return "qlora-mi355x 0.1.0 (gfx950)"; }
 
 int qlora_timing_begin(uint32_t mask) {
-  g_timer.clear();
+  for (auto& u : g_timer.used) u.clear();
+  g_timer.cursor = 0;
   g_timer.mask = mask;
   g_timer.on = true;
   return QLORA_OK;
@@ -227,14 +246,15 @@ int qlora_timing_end(void) {
 int qlora_timing_read(int kernel_class, double* total_ms, int64_t* launches) {
   if (kernel_class < 0 || kernel_class >= QLORA_K_COUNT) return QLORA_E_INVALID;
   double sum = 0.0;
-  for (auto& p : g_timer.ev[kernel_class]) {
+  for (size_t idx : g_timer.used[kernel_class]) {
+    const auto& p = g_timer.pool[idx];
     if (hipEventSynchronize(p.second) != hipSuccess) return QLORA_E_HIP;
     float ms = 0.0f;
     if (hipEventElapsedTime(&ms, p.first, p.second) != hipSuccess) return QLORA_E_HIP;
     sum += ms;
   }
   if (total_ms) *total_ms = sum;
-  if (launches) *launches = (int64_t)g_timer.ev[kernel_class].size();
+  if (launches) *launches = (int64_t)g_timer.used[kernel_class].size();
   return QLORA_OK;
 }
 
@@ -321,9 +341,12 @@ int qlora_linear_fwd(const qlora_bf16* X, int64_t M, int64_t d, const qlora_nf4d
   const bool lora = r > 0 && s != 0.0f;
 
   if (L.gemv) {
+    // T planes (the adapter class), then the dequant-GEMV that sums them
+    if (r > 0 && (lora || T_out != nullptr))
+      QL_RUN(QLORA_K_ADAPTER, hs, launch_gemv_tdown(X, (int)M, d, A, (int)r, Tpart, hs));
     QL_RUN(QLORA_K_GEMV, hs,
            launch_gemv_fwd(X, (int)M, d, W->codes, W->scale8, W->scale2, o, A, B, (int)r, s, Y,
-                           T_out, Tpart, host_codebook(W->fmt), hs));
+                           T_out, Tpart, host_codebook(W->fmt), hs, nullptr, 0, nullptr, false));
     return QLORA_OK;
   }
   uint16_t* sT = reinterpret_cast<uint16_t*>(w + L.sT);
@@ -362,9 +385,12 @@ int qlora_linear_fwd_multi(const qlora_bf16* X, int64_t M, int64_t d, const qlor
   if ((st = device_status())) return st;
   hipStream_t hs = (hipStream_t)stream;
   float* Tpart = reinterpret_cast<float*>(static_cast<char*>(ws) + L.Tpart);
+  QL_RUN(QLORA_K_ADAPTER, hs,
+         launch_gemv_tdown(X, (int)M, d, A, (int)r, Tpart, hs, d_adapter, (int)n_adapters));
   QL_RUN(QLORA_K_GEMV, hs,
          launch_gemv_fwd(X, (int)M, d, W->codes, W->scale8, W->scale2, o, A, B, (int)r, 0.0f, Y,
-                         T_out, Tpart, host_codebook(W->fmt), hs, d_adapter, (int)n_adapters, s));
+                         T_out, Tpart, host_codebook(W->fmt), hs, d_adapter, (int)n_adapters, s,
+                         false));
   return QLORA_OK;
 }
 

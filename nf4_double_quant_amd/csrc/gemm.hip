@@ -54,7 +54,7 @@ hipError_t launch_reduce_planes(const ReduceJob& a, const ReduceJob& b, hipStrea
   };
   const int ba = blocks(a.count), bb = blocks(b.count);
   if (ba + bb == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_reduce_planes, dim3((unsigned)(ba + bb)), dim3(256), 0, st, a, b, ba);
+  launch(k_reduce_planes, dim3((unsigned)(ba + bb)), dim3(256), 0, st, a, b, ba);
   return hipGetLastError();
 }
 
@@ -62,7 +62,7 @@ hipError_t launch_fill_zero_bf16(uint16_t* y, int64_t n, hipStream_t st) {
   if (n == 0) return hipSuccess;
   int64_t blocks = (n + 255) / 256;
   if (blocks > 8192) blocks = 8192;
-  hipLaunchKernelGGL(k_fill_zero_bf16, dim3((unsigned)blocks), dim3(256), 0, st, y, n);
+  launch(k_fill_zero_bf16, dim3((unsigned)blocks), dim3(256), 0, st, y, n);
   return hipGetLastError();
 }
 

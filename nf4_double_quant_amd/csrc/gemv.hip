@@ -554,19 +554,25 @@ bool gemv_fits(int64_t M, int64_t d, int64_t r) {
   return gemv_plan((int)M, d, (int)r, r > 0, r > 0).lds <= kGemvMaxLds;
 }
 
+hipError_t launch_gemv_tdown(const uint16_t* X, int M, int64_t d, const uint16_t* A, int r,
+                             float* Tpart, hipStream_t st, const int32_t* adapter, int n_ad) {
+  if (r <= 0) return hipSuccess;
+  launch(k_lora_down_small, dim3(gemv_tsplits(d), (r + 63) / 64, adapter != nullptr ? M : 1),
+         dim3(256), 0, st, X, M, d, A, r, Tpart, adapter, n_ad);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemv_fwd(const uint16_t* X, int M, int64_t d, const uint8_t* codes,
                            const uint8_t* scale8, const float* scale2, int64_t o,
                            const uint16_t* A, const uint16_t* B, int r, float s, uint16_t* Y,
                            float* T_out, float* Tpart, const Codebook& cb, hipStream_t st,
-                           const int32_t* adapter, int n_ad, const float* s_ad) {
+                           const int32_t* adapter, int n_ad, const float* s_ad, bool tdown) {
   const int ts = gemv_tsplits(d);
   const bool multi = adapter != nullptr;
   if (multi && (n_ad < 1 || n_ad > kMaxAdapters || s_ad == nullptr)) return hipErrorInvalidValue;
   const int rr = (r > 0 && (multi || s != 0.0f || T_out != nullptr)) ? r : 0;
-  if (rr > 0) {
-    hipLaunchKernelGGL(k_lora_down_small, dim3(ts, (rr + 63) / 64, multi ? M : 1), dim3(256), 0, st,
-                       X, M, d, A, rr, Tpart, adapter, n_ad);
-    hipError_t e = hipGetLastError();
+  if (rr > 0 && tdown) {
+    hipError_t e = launch_gemv_tdown(X, M, d, A, rr, Tpart, st, adapter, n_ad);
     if (e != hipSuccess) return e;
   }
   const unsigned grid = (unsigned)((o + 15) / 16);
@@ -578,10 +584,10 @@ hipError_t launch_gemv_fwd(const uint16_t* X, int M, int64_t d, const uint8_t* c
   for (int i = 0; multi && i < n_ad; ++i) p.s_ad[i] = s_ad[i];
   const size_t lds = (size_t)g.lds;
   switch (g.mx) {
-    case 1: hipLaunchKernelGGL(k_gemv<1>, dim3(grid), dim3(64 * g.nw), lds, st, p); break;
-    case 2: hipLaunchKernelGGL(k_gemv<2>, dim3(grid), dim3(64 * g.nw), lds, st, p); break;
-    case 4: hipLaunchKernelGGL(k_gemv<4>, dim3(grid), dim3(64 * g.nw), lds, st, p); break;
-    default: hipLaunchKernelGGL(k_gemv<16>, dim3(grid), dim3(64 * g.nw), lds, st, p); break;
+    case 1: launch(k_gemv<1>, dim3(grid), dim3(64 * g.nw), lds, st, p); break;
+    case 2: launch(k_gemv<2>, dim3(grid), dim3(64 * g.nw), lds, st, p); break;
+    case 4: launch(k_gemv<4>, dim3(grid), dim3(64 * g.nw), lds, st, p); break;
+    default: launch(k_gemv<16>, dim3(grid), dim3(64 * g.nw), lds, st, p); break;
   }
   return hipGetLastError();
 }

@@ -2,9 +2,34 @@
 // given stream and returns the launch status; shapes are checked by callers.
 #pragma once
 
+#include <hip/hip_ext.h>
+
 #include "common.h"
 
 namespace qlora {
+
+// Every kernel of the library is launched through launch().  While the
+// timing diagnostics have armed this thread's event pair (the launches of
+// one timed call), the first kernel records the start event and every kernel
+// the stop event, at the dispatch's own begin and end; otherwise it is a
+// plain launch.
+struct LaunchEvents {
+  hipEvent_t start, stop;
+  bool fired;
+};
+LaunchEvents*& armed_launch_events();
+
+template <typename K, typename... Args>
+inline void launch(K kernel, dim3 grid, dim3 block, size_t shmem, hipStream_t st, Args... args) {
+  LaunchEvents* ev = armed_launch_events();
+  if (ev == nullptr) {
+    hipLaunchKernelGGL(kernel, grid, block, shmem, st, args...);
+    return;
+  }
+  hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)shmem, st, ev->start, ev->stop, 0u, args...);
+  ev->start = nullptr;
+  ev->fired = true;
+}
 
 
 // fmt: the 16-entry table of the codes (host_codebook(fmt), with its
@@ -78,12 +103,17 @@ bool gemv_fits(int64_t M, int64_t d, int64_t r);
 // adapter != null: one adapter per token, A [n_ad][d][r], B [n_ad][r][o],
 // scales s_ad[n_ad] (host); an index outside [0, n_ad) selects no adapter.
 constexpr int kMaxAdapters = 64;
+// The T planes of the few-token kernel (k_lora_down_small): Tpart
+// [gemv_tsplits(d)][M][r]; launch_gemv_fwd with tdown = false then skips them.
+hipError_t launch_gemv_tdown(const uint16_t* X, int M, int64_t d, const uint16_t* A, int r,
+                             float* Tpart, hipStream_t st, const int32_t* adapter = nullptr,
+                             int n_ad = 0);
 hipError_t launch_gemv_fwd(const uint16_t* X, int M, int64_t d, const uint8_t* codes,
                            const uint8_t* scale8, const float* scale2, int64_t o,
                            const uint16_t* A, const uint16_t* B, int r, float s, uint16_t* Y,
                            float* T_out, float* Tpart, const Codebook& cb, hipStream_t st,
                            const int32_t* adapter = nullptr, int n_ad = 0,
-                           const float* s_ad = nullptr);
+                           const float* s_ad = nullptr, bool tdown = true);
 
 // Adapter merge: W_out[n][k] = fl32(ŵ[n][k] + fl32(s·Σ_j A[k][j]·B[j][n])),
 // the rank sum by fp32 FMAs in increasing j.  d % 64 == 0, o % 8 == 0.

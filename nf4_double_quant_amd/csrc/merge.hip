@@ -139,7 +139,7 @@ hipError_t launch_merge(const uint8_t* codes, const uint8_t* scale8, const float
                         float* W_out, const Codebook& cb, hipStream_t st) {
   if (o == 0 || d == 0) return hipSuccess;
   const dim3 grid((unsigned)((d + kMgK - 1) / kMgK), (unsigned)((o + kMgN - 1) / kMgN));
-  hipLaunchKernelGGL(k_merge, grid, dim3(256), 0, st, codes, scale8, scale2, o, d, A, B, r, s,
+  launch(k_merge, grid, dim3(256), 0, st, codes, scale8, scale2, o, d, A, B, r, s,
                      W_out, cb);
   return hipGetLastError();
 }

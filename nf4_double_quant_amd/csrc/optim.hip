@@ -120,7 +120,7 @@ hipError_t launch_adamw(float* p, uint16_t* p16, const uint16_t* g, float* m, fl
                         const AdamwConsts& k, hipStream_t st) {
   if (n == 0) return hipSuccess;
   const int64_t quads = (n + 3) / 4;
-  hipLaunchKernelGGL(k_adamw, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, st, p, p16, g, m,
+  launch(k_adamw, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, st, p, p16, g, m,
                      v, n, k);
   return hipGetLastError();
 }

@@ -503,9 +503,9 @@ hipError_t launch_qgemm(bool trans_w, const uint16_t* A, int64_t lda, const uint
               cb};
   const unsigned tiles = (unsigned)(((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN));
   if (trans_w)
-    hipLaunchKernelGGL((k_qgemm<true, kWaves>), dim3(tiles), dim3(64 * kWaves), 0, st, p);
+    launch(k_qgemm<true, kWaves>, dim3(tiles), dim3(64 * kWaves), 0, st, p);
   else
-    hipLaunchKernelGGL((k_qgemm<false, kWaves>), dim3(tiles), dim3(64 * kWaves), 0, st, p);
+    launch(k_qgemm<false, kWaves>, dim3(tiles), dim3(64 * kWaves), 0, st, p);
   return hipGetLastError();
 }
 

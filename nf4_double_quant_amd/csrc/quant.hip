@@ -417,9 +417,9 @@ hipError_t launch_dq_variant(const float* W, int64_t n, uint8_t* scale8, float* 
   const int64_t nb = (n + kBlock - 1) / kBlock;
   const int64_t ng = (nb + kGroup - 1) / kGroup;
   if (ng == 0 || dq == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_dq_psum, dim3((unsigned)ng), dim3(256), 0, st, W, n, psum);
-  hipLaunchKernelGGL(k_dq_mean, dim3(1), dim3(64), 0, st, psum, ng, nb, scale2);
-  hipLaunchKernelGGL(k_dq_second, dim3((unsigned)ng), dim3(256), 0, st, W, n, scale8, scale2, dq);
+  launch(k_dq_psum, dim3((unsigned)ng), dim3(256), 0, st, W, n, psum);
+  launch(k_dq_mean, dim3(1), dim3(64), 0, st, psum, ng, nb, scale2);
+  launch(k_dq_second, dim3((unsigned)ng), dim3(256), 0, st, W, n, scale8, scale2, dq);
   return hipGetLastError();
 }
 
@@ -430,7 +430,7 @@ hipError_t launch_quantize(const float* W, int64_t n, uint8_t* codes, uint8_t* s
   if (ng == 0) return hipSuccess;
   const EncodeGuide& eg = host_encode_guide(fmt);
   if (eg.zero_cell < 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_quantize, dim3((unsigned)ng), dim3(256), 0, st, W, n, codes, scale8,
+  launch(k_quantize, dim3((unsigned)ng), dim3(256), 0, st, W, n, codes, scale8,
                      scale2, flags, host_codebook(fmt), eg);
   return hipGetLastError();
 }
@@ -443,10 +443,10 @@ hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scale8, const flo
   int64_t blocks = (n8 + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   if (bf16)
-    hipLaunchKernelGGL(k_dequant<true>, dim3((unsigned)blocks), dim3(256), 0, st, codes, scale8,
+    launch(k_dequant<true>, dim3((unsigned)blocks), dim3(256), 0, st, codes, scale8,
                        scale2, n, out, cb, dq);
   else
-    hipLaunchKernelGGL(k_dequant<false>, dim3((unsigned)blocks), dim3(256), 0, st, codes, scale8,
+    launch(k_dequant<false>, dim3((unsigned)blocks), dim3(256), 0, st, codes, scale8,
                        scale2, n, out, cb, dq);
   return hipGetLastError();
 }

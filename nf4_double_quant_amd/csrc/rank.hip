@@ -407,9 +407,9 @@ hipError_t launch_rank_down(bool q_rowmajor_k, const uint16_t* P, int64_t M, int
   dim3 grid((unsigned)((M + kDownRows - 1) / kDownRows), (unsigned)rank_down_splits(K),
             (unsigned)((r + 63) / 64));
   if (q_rowmajor_k)
-    hipLaunchKernelGGL(k_rank_down<true>, grid, dim3(256), 0, st, P, M, K, Q, r, part);
+    launch(k_rank_down<true>, grid, dim3(256), 0, st, P, M, K, Q, r, part);
   else
-    hipLaunchKernelGGL(k_rank_down<false>, grid, dim3(256), 0, st, P, M, K, Q, r, part);
+    launch(k_rank_down<false>, grid, dim3(256), 0, st, P, M, K, Q, r, part);
   return hipGetLastError();
 }
 
@@ -418,7 +418,7 @@ hipError_t launch_rank_grads(RankGradJob a, RankGradJob b, int r, int64_t M, hip
   b.tiles = b.P > 0 ? (int)((b.P + kGradP - 1) / kGradP) : 0;
   if (a.tiles + b.tiles == 0 || r == 0 || M == 0) return hipSuccess;
   dim3 grid((unsigned)(a.tiles + b.tiles), (unsigned)rank_grad_splits(M), (unsigned)((r + 63) / 64));
-  hipLaunchKernelGGL(k_rank_grad, grid, dim3(256), 0, st, a, b, r, M);
+  launch(k_rank_grad, grid, dim3(256), 0, st, a, b, r, M);
   return hipGetLastError();
 }
 
