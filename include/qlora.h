@@ -63,6 +63,8 @@ extern "C" {
 #define QLORA_MAX_RANK 256  /* largest LoRA rank r accepted                  */
 #define QLORA_MAX_DIM (1LL << 20)       /* largest d and o of a linear layer  */
 #define QLORA_MAX_WEIGHTS (1LL << 31)   /* largest o*d of a linear layer      */
+#define QLORA_MAX_TOKENS (1LL << 26)    /* largest M of a linear layer        */
+#define QLORA_MAX_ELEMENTS (1LL << 40)  /* largest n of the elementwise calls */
 #define QLORA_MAX_MULTI_TOKENS 16       /* largest M of qlora_linear_fwd_multi */
 #define QLORA_MAX_ADAPTERS 64           /* largest adapter count of the same   */
 #define QLORA_NOALLOC_SCRATCH_BYTES (64LL << 20)  /* static scratch of qlora_linear_bwd_noalloc */
@@ -70,9 +72,11 @@ extern "C" {
 typedef enum {
   QLORA_OK = 0,
   QLORA_E_INVALID = 1,    /* null pointer where one is required, bad enum, n < 0 */
-  QLORA_E_SHAPE = 2,      /* d % 64 != 0, r out of range or not a multiple of 8,
-                             negative sizes, n != o*d, d or o above
-                             QLORA_MAX_DIM, o*d above QLORA_MAX_WEIGHTS      */
+  QLORA_E_SHAPE = 2,      /* d % 64 != 0, o % 8 != 0, r out of range or not a
+                             multiple of 8, negative sizes, n != o*d, d or o
+                             above QLORA_MAX_DIM, o*d above QLORA_MAX_WEIGHTS,
+                             M above QLORA_MAX_TOKENS, n of the quantizer,
+                             dequantizer or optimizer above QLORA_MAX_ELEMENTS */
   QLORA_E_ALIGN = 3,      /* a tensor pointer is not 16-byte aligned          */
   QLORA_E_WORKSPACE = 4,  /* ws_bytes below qlora_workspace_bytes()          */
   QLORA_E_NO_DEVICE = 5,  /* no HIP device visible to the process            */
@@ -173,7 +177,8 @@ const char* qlora_version(void);
  * (QLoRA-074 §三 procedure: blockwise NF4 quantize with block 64, then
  * quantize the first-level constants with block 256; §二 NF4 and double
  * quantization).
- *   W      device fp32[n], any values; n >= 0 (n = 0 is a no-op).
+ *   W      device fp32[n], any values; 0 <= n <= QLORA_MAX_ELEMENTS (n = 0
+ *          is a no-op).
  *   out    view of caller buffers sized by qlora_quant_sizes(n); out->n must
  *          equal n.  Overwritten entirely.
  *   d_flags device int32 or NULL.  If any weight is NaN or ±Inf, bit 0 is set
@@ -223,7 +228,9 @@ int qlora_dequant(const qlora_nf4dq* q, int out_dtype, void* out, void* stream);
  *   ws     device workspace of at least qlora_workspace_bytes(QLORA_OP_FWD,...)
  * Products use bf16 operands (the dequantized weight rounded to bf16) with
  * fp32 accumulation; Y is rounded to bf16 once.  M == 0 is a no-op.
- * 0 <= r <= 256 and r % 8 == 0; A and B may be NULL only if r == 0. */
+ * 0 <= r <= 256, r % 8 == 0, o % 8 == 0 and M <= QLORA_MAX_TOKENS (eight
+ * bf16 values are the 16-byte unit the kernels stream rows of A, B and Y
+ * in); A and B may be NULL only if r == 0. */
 int qlora_linear_fwd(const qlora_bf16* X, int64_t M, int64_t d,
                      const qlora_nf4dq* W, int64_t o,
                      const qlora_bf16* A, const qlora_bf16* B, int64_t r, float s,

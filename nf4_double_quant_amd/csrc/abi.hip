@@ -16,7 +16,8 @@ namespace {
 
 constexpr int64_t kAlign = 256;
 
-inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+// a >= 0, b > 0; no intermediate overflows, also for a = INT64_MAX
+inline int64_t cdiv(int64_t a, int64_t b) { return a / b + (a % b != 0); }
 inline int64_t up(int64_t a) { return cdiv(a, kAlign) * kAlign; }
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 inline int64_t clampi(int64_t v, int64_t lo, int64_t hi) { return v < lo ? lo : (v > hi ? hi : v); }
@@ -151,6 +152,7 @@ int check_quant_view(const qlora_nf4dq* q, bool allow_dq = false) {
 
 int check_linear_shapes(int64_t M, int64_t d, int64_t o, int64_t r, const qlora_nf4dq* W) {
   if (M < 0 || d <= 0 || o <= 0 || r < 0) return QLORA_E_SHAPE;
+  if (M > QLORA_MAX_TOKENS) return QLORA_E_SHAPE;
   // the kernels address a weight tensor and a 512-row activation tile with
   // 32-bit offsets
   if (d > QLORA_MAX_DIM || o > QLORA_MAX_DIM || o * d > QLORA_MAX_WEIGHTS) return QLORA_E_SHAPE;
@@ -208,6 +210,7 @@ int qlora_codebook(int fmt, float* out) {
 
 size_t qlora_workspace_bytes(int op, int64_t M, int64_t d, int64_t o, int64_t r) {
   if (M < 0 || d < 0 || o < 0 || r < 0 || r > QLORA_MAX_RANK) return 0;
+  if (M > QLORA_MAX_TOKENS || d > QLORA_MAX_DIM || o > QLORA_MAX_DIM) return 0;
   if (op == QLORA_OP_FWD) return (size_t)fwd_layout(M, d, o, r).total;
   if (op == QLORA_OP_BWD) return (size_t)bwd_layout(M, d, o, r).total;
   return 0;
@@ -217,7 +220,7 @@ const char* qlora_strerror(int status) {
   switch (status) {
     case QLORA_OK: return "ok";
     case QLORA_E_INVALID: return "invalid argument";
-    case QLORA_E_SHAPE: return "unsupported shape (need d % 64 == 0, o % 8 == 0, 0 <= r <= 256, r % 8 == 0, n == o*d, d and o <= 2^20, o*d <= 2^31)";
+    case QLORA_E_SHAPE: return "unsupported shape (need d % 64 == 0, o % 8 == 0, 0 <= r <= 256, r % 8 == 0, n == o*d, d and o <= 2^20, o*d <= 2^31, M <= 2^26, n <= 2^40)";
     case QLORA_E_ALIGN: return "tensor pointer not 16-byte aligned";
     case QLORA_E_WORKSPACE: return "workspace too small";
     case QLORA_E_NO_DEVICE: return "no HIP device available";
@@ -264,6 +267,7 @@ int qlora_quantize_nf4_dq(const float* W, int64_t n, const qlora_nf4dq* out, int
   if (n > 0 && W == nullptr) return QLORA_E_INVALID;
   int st = check_quant_view(out);
   if (st) return st;
+  if (n > QLORA_MAX_ELEMENTS) return QLORA_E_SHAPE;
   if (out->n != n) return QLORA_E_SHAPE;
   if (!aligned16(W)) return QLORA_E_ALIGN;
   if (n == 0) return QLORA_OK;
@@ -292,11 +296,11 @@ int qlora_quantize_nf4_dq_ws(const float* W, int64_t n, const qlora_nf4dq* out, 
   if (n > 0 && W == nullptr) return QLORA_E_INVALID;
   int st = check_quant_view(out, true);
   if (st) return st;
-  if (out->n != n) return QLORA_E_SHAPE;
+  if (out->n != n || n > QLORA_MAX_ELEMENTS) return QLORA_E_SHAPE;
   if (!aligned16(W) || !aligned16(ws)) return QLORA_E_ALIGN;
   int64_t need = 0;
   qlora_quant_sizes_dq(n, out->dq, nullptr, nullptr, nullptr, &need);
-  if ((int64_t)ws_bytes < need || (need > 0 && ws == nullptr)) return QLORA_E_WORKSPACE;
+  if (ws_bytes < (size_t)need || (need > 0 && ws == nullptr)) return QLORA_E_WORKSPACE;
   if (n == 0) return QLORA_OK;
   if ((st = device_status())) return st;
   hipStream_t hs = (hipStream_t)stream;
@@ -311,6 +315,7 @@ int qlora_dequant(const qlora_nf4dq* q, int out_dtype, void* out, void* stream) 
   int st = check_quant_view(q, true);
   if (st) return st;
   if (out_dtype != QLORA_F32 && out_dtype != QLORA_BF16) return QLORA_E_INVALID;
+  if (q->n > QLORA_MAX_ELEMENTS) return QLORA_E_SHAPE;
   if (q->n > 0 && out == nullptr) return QLORA_E_INVALID;
   if (!aligned16(out)) return QLORA_E_ALIGN;
   if (q->n == 0) return QLORA_OK;
@@ -415,6 +420,7 @@ int check_adamw(const float* p, const qlora_bf16* p16, const qlora_bf16* g, cons
   if (n > 0 && (p == nullptr || g == nullptr || m == nullptr || v == nullptr)) return QLORA_E_INVALID;
   if (!aligned16(p) || !aligned16(p16) || !aligned16(g) || !aligned16(m) || !aligned16(v))
     return QLORA_E_ALIGN;
+  if (n > QLORA_MAX_ELEMENTS) return QLORA_E_SHAPE;
   return QLORA_OK;
 }
 }  // namespace
