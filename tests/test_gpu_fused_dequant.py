@@ -124,3 +124,13 @@ def test_gemv_decode_gate_weight_one_hot():
     _gemv_columns(W, "nf4", 16, cols)
     _gemv_columns(W, "nf4", 13, cols[:13])
     _gemv_columns(W, "nf4", 1, cols[::5])
+
+
+def test_gemv_decode_down_weight_one_hot():
+    """The down projection (d = 11008: 172 blocks per row, 43 groups of four):
+    one-hot columns at the first, last and group-boundary positions."""
+    wl = synth.WORKLOADS["decode_mlp_7b"]
+    p = next(x for x in wl.projs if x.name == "down")
+    W = synth.normal_f32((p.o, p.d), wl.w_std, [wl.wid, synth.PROJ_IDS[p.name], synth.T_W])
+    cols = [0, 63, 4095, 4096, 4159, 8191, 8192, 8255, 10943, 10944, 11007]
+    _gemv_columns(W, "nf4", 1, cols)

@@ -190,6 +190,15 @@ def test_few_token_path(M, d, o, r):
     full_parity(M, d, o, r, 2.0, seed=1000 + M * 31 + d + o + r)
 
 
+@pytest.mark.parametrize("d,o,r", [(8192, 264, 16), (12288, 72, 64), (4160, 1000, 8),
+                                   (640, 40, 72), (13312, 16, 8)])
+def test_one_token_shapes(d, o, r):
+    """One token at long rows (up to 12288 and past it), a ragged count of
+    64-weight blocks per row, and ranks up to the largest the few-token
+    kernel's epilogue sees in practice and beyond."""
+    full_parity(1, d, o, r, 2.0, seed=2000 + d + o + r)
+
+
 @pytest.mark.parametrize("proj", ["gate", "down"])
 def test_decode_mlp_7b_full(proj):
     """7B-style MLP weights at decode sizes M = 1, 4, 16, rank 16: every output."""
