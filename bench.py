@@ -330,6 +330,8 @@ def main():
         if mf.get("source_hash") == source_hash(PMC_KERNELS["k_qgemm"][1]):
             roofline["mfma_busy_frac"] = mf.get("mfma_busy_frac")
 
+    roofline["context_plain_bf16_gemm"] = plain_gemm_reference(torch, X, W, args.steps)
+
     breakdown = {name: {"ms_per_step": round(ms / nb, 4), "launches_per_step": n / nb}
                  for name, (ms, n) in per_class.items() if n}
 
@@ -565,6 +567,30 @@ def bench_decode(args, qb, torch, np, synth, dev):
             "weight_sets_cycled": len(sets), "peak_GBps": PEAK_HBM_GBPS, "roofline": roofline, **res}
 
 
+def plain_gemm_reference(torch, X, W, reps):
+    """Context for the roofline, not a target: the same-shape product X·Wᵀ as a
+    plain bf16 GEMM through torch (hipBLASLt on this system), no dequantization
+    and no adapter, timed with events around `reps` back-to-back launches."""
+    Wb = W.to(torch.bfloat16)
+    y = torch.nn.functional.linear(X, Wb)
+    for _ in range(3):
+        torch.nn.functional.linear(X, Wb)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        torch.nn.functional.linear(X, Wb)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    M, d = X.shape
+    o = Wb.shape[0]
+    tf = 2 * M * d * o / (us * 1e-6) / 1e12
+    del Wb, y
+    return {"op": "torch.nn.functional.linear, bf16 (hipBLASLt)", "shape_MNK": [M, o, d],
+            "us": round(us, 2), "TFLOP/s": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+
+
 def decode_roofline(qb, wl, m1):
     """HBM roofline of the few-token dequant-GEMV at 1 token: algorithmic
     bytes per launch (averaged over gate, up and down) over its average
@@ -619,8 +645,20 @@ def bench_blocks(qb, torch, synth, dev, steps=5, warmup=2):
                     qb.qlora_quantize_nf4_dq(W, check_finite=False, out=q)
             e1.record()
             torch.cuda.synchronize()
+            us_sep = e0.elapsed_time(e1) * 1e3 / steps
+            # the same seven tensors in one grouped launch
+            for _ in range(2):
+                qb.qlora_quantize_nf4_dq_grouped(Ws, check_finite=False, outs=qs)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(steps):
+                qb.qlora_quantize_nf4_dq_grouped(Ws, check_finite=False, outs=qs)
+            e1.record()
+            torch.cuda.synchronize()
             us = e0.elapsed_time(e1) * 1e3 / steps
-            res["quantize_all"] = {"us": round(us, 1), "weights": n_total, "bytes": quant_bytes,
+            res["quantize_all"] = {"us": round(us, 1), "launch": "one grouped launch",
+                                   "us_one_launch_per_tensor": round(us_sep, 1),
+                                   "weights": n_total, "bytes": quant_bytes,
                                    "GBps": round(quant_bytes / (us * 1e-6) / 1e9, 1),
                                    "frac_of_hbm": round(quant_bytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)}
         del Ws

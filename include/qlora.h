@@ -66,6 +66,7 @@ extern "C" {
 #define QLORA_MAX_TOKENS (1LL << 26)    /* largest M of a linear layer        */
 #define QLORA_MAX_ELEMENTS (1LL << 40)  /* largest n of the elementwise calls */
 #define QLORA_MAX_MULTI_TOKENS 16       /* largest M of qlora_linear_fwd_multi */
+#define QLORA_MAX_GROUPED 16            /* most tensors of qlora_quantize_nf4_dq_grouped */
 #define QLORA_MAX_ADAPTERS 64           /* largest adapter count of the same   */
 #define QLORA_NOALLOC_SCRATCH_BYTES (64LL << 20)  /* static scratch of qlora_linear_bwd_noalloc */
 
@@ -194,6 +195,19 @@ const char* qlora_version(void);
  * (ties to the lower), 0 if step is 0. */
 int qlora_quantize_nf4_dq(const float* W, int64_t n, const qlora_nf4dq* out,
                           int32_t* d_flags, void* stream);
+
+/* The same quantization for several tensors in one launch (the procedure of
+ * QLoRA-074 §三 applied to each tensor: blockwise NF4 with block 64, then the
+ * constants with block 256).  Tensor k is W[k] (device fp32[outs[k].n]) and
+ * its outputs are the buffers of outs[k], exactly as qlora_quantize_nf4_dq(
+ * W[k], outs[k].n, &outs[k], d_flags, stream) would write them; groups never
+ * span two tensors.  W and outs are host arrays of `count` entries,
+ * 0 <= count <= QLORA_MAX_GROUPED (0 is a no-op); every view must use the
+ * same table (fmt) and QLORA_DQ_UINT8; an entry with n = 0 is skipped.
+ * d_flags as for qlora_quantize_nf4_dq (one word for all tensors).  Errors
+ * as for qlora_quantize_nf4_dq, checked for every entry before any launch. */
+int qlora_quantize_nf4_dq_grouped(const float* const* W, const qlora_nf4dq* outs, int count,
+                                  int32_t* d_flags, void* stream);
 
 /* The quantizer for any second-level variant out->dq (QLORA_DQ_UINT8 gives
  * exactly qlora_quantize_nf4_dq).  The codes are those of the default scheme

@@ -70,6 +70,7 @@ def lib() -> ctypes.CDLL:
     L.qlora_version.restype = ctypes.c_char_p
     L.qlora_quantize_nf4_dq.argtypes = [vp, i64, P(_NF4DQ), vp, vp]
     L.qlora_quantize_nf4_dq_ws.argtypes = [vp, i64, P(_NF4DQ), vp, vp, sz, vp]
+    L.qlora_quantize_nf4_dq_grouped.argtypes = [P(vp), P(_NF4DQ), i32, vp, vp]
     L.qlora_quant_sizes_dq.argtypes = [i64, i32, P(i64), P(i64), P(i64), P(i64)]
     L.qlora_dequant.argtypes = [P(_NF4DQ), i32, vp, vp]
     L.qlora_linear_fwd.argtypes = [vp, i64, i64, P(_NF4DQ), i64, vp, vp, i64, ctypes.c_float,
@@ -86,7 +87,8 @@ def lib() -> ctypes.CDLL:
     L.qlora_timing_begin.argtypes = [ctypes.c_uint32]
     L.qlora_timing_read.argtypes = [i32, P(ctypes.c_double), P(i64)]
     for name in ("qlora_quant_sizes", "qlora_quant_sizes_dq", "qlora_quantize_nf4_dq_ws",
-                 "qlora_codebook", "qlora_quantize_nf4_dq", "qlora_dequant",
+                 "qlora_codebook", "qlora_quantize_nf4_dq", "qlora_quantize_nf4_dq_grouped",
+                 "qlora_dequant",
                  "qlora_linear_fwd", "qlora_linear_bwd", "qlora_linear_bwd_noalloc",
                  "qlora_linear_fwd_multi",
                  "qlora_merge_adapter", "qlora_adamw_step", "qlora_paged_adamw_step",
@@ -309,6 +311,50 @@ def qlora_quantize_nf4_dq(W, check_finite: bool = True, out: QuantizedWeight | N
         raise QloraError(QLORA_E_NONFINITE, "qlora_quantize_nf4_dq")
     q.flags = flags
     return q
+
+
+QLORA_MAX_GROUPED = 16
+
+
+def qlora_quantize_nf4_dq_grouped(Ws, check_finite: bool = True, outs=None,
+                                  fmt="nf4") -> list:
+    """Blockwise 4-bit + double quantization of several fp32 device tensors
+    (one table, the default code of the constants) in one launch; the result
+    for each equals qlora_quantize_nf4_dq of that tensor.  `outs` reuses
+    earlier results of the same sizes.  With check_finite the call waits and
+    raises on NaN/Inf in any input."""
+    torch = _torch()
+    Ws = list(Ws)
+    if len(Ws) > QLORA_MAX_GROUPED:
+        raise ValueError(f"at most {QLORA_MAX_GROUPED} tensors per grouped call")
+    if outs is not None and len(outs) != len(Ws):
+        raise ValueError("outs must match Ws one to one")
+    if not Ws:
+        return []
+    dev = Ws[0].device
+    qs = []
+    for k, W in enumerate(Ws):
+        _need(W, torch.float32, f"Ws[{k}]", dev)
+        _tensor(W, f"Ws[{k}]")
+        if outs is None:
+            qs.append(_alloc_quantized(W.numel(), W.shape, W.device, _fmt_code(fmt)))
+        else:
+            o = outs[k]
+            if o.n != W.numel():
+                raise ValueError(f"outs[{k}] holds a different number of weights")
+            if o.dq != 0:
+                raise ValueError("the grouped quantizer writes the default code of the constants")
+            qs.append(o)
+    flags = torch.zeros(1, dtype=torch.int32, device=dev)
+    views = (_NF4DQ * len(qs))(*[q.view() for q in qs])
+    ptrs = (ctypes.c_void_p * len(Ws))(*[_ptr(W) for W in Ws])
+    _check(lib().qlora_quantize_nf4_dq_grouped(ptrs, views, len(Ws), _ptr(flags), _stream(dev)),
+           "qlora_quantize_nf4_dq_grouped")
+    if check_finite and int(flags.item()) & 1:
+        raise QloraError(QLORA_E_NONFINITE, "qlora_quantize_nf4_dq_grouped")
+    for q in qs:
+        q.flags = flags
+    return qs
 
 
 def qlora_stack_rows(parts) -> QuantizedWeight:

@@ -277,6 +277,34 @@ int qlora_quantize_nf4_dq(const float* W, int64_t n, const qlora_nf4dq* out, int
   return QLORA_OK;
 }
 
+int qlora_quantize_nf4_dq_grouped(const float* const* W, const qlora_nf4dq* outs, int count,
+                                  int32_t* d_flags, void* stream) {
+  if (count < 0 || count > QLORA_MAX_GROUPED) return QLORA_E_INVALID;
+  if (count == 0) return QLORA_OK;
+  if (W == nullptr || outs == nullptr) return QLORA_E_INVALID;
+  QuantJobs jobs{};
+  int64_t g0 = 0;
+  for (int k = 0; k < count; ++k) {
+    const qlora_nf4dq& o = outs[k];
+    int st = check_quant_view(&o);
+    if (st) return st;
+    if (o.fmt != outs[0].fmt) return QLORA_E_INVALID;
+    if (o.n > QLORA_MAX_ELEMENTS) return QLORA_E_SHAPE;
+    if (o.n > 0 && W[k] == nullptr) return QLORA_E_INVALID;
+    if (!aligned16(W[k])) return QLORA_E_ALIGN;
+    jobs.j[k] = QuantJob{W[k], o.codes, o.scale8, o.scale2, o.n, g0};
+    g0 += cdiv(o.n, QLORA_BLOCK * QLORA_GROUP);
+  }
+  if (g0 > 0x7FFFFFFF) return QLORA_E_SHAPE;
+  jobs.count = count;
+  if (g0 == 0) return QLORA_OK;
+  int st = device_status();
+  if (st) return st;
+  QL_RUN(QLORA_K_QUANTIZE, (hipStream_t)stream,
+         launch_quantize_grouped(jobs, d_flags, outs[0].fmt, (hipStream_t)stream));
+  return QLORA_OK;
+}
+
 int qlora_quant_sizes_dq(int64_t n, int dq, int64_t* codes_bytes, int64_t* scale8_bytes,
                          int64_t* scale2_bytes, int64_t* ws_bytes) {
   if (n < 0 || dq < QLORA_DQ_UINT8 || dq > QLORA_DQ_FP8_MEAN) return QLORA_E_INVALID;

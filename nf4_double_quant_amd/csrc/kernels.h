@@ -36,6 +36,21 @@ inline void launch(K kernel, dim3 grid, dim3 block, size_t shmem, hipStream_t st
 // host_encode_guide(fmt)); hipErrorInvalidValue when the guide is unusable.
 hipError_t launch_quantize(const float* W, int64_t n, uint8_t* codes, uint8_t* scale8,
                            float* scale2, int32_t* flags, int fmt, hipStream_t st);
+// Several tensors of one table in one launch: job k covers workgroups
+// [g0, g0 + ceil(n/16384)), the jobs in order with g0 the running sum.
+constexpr int kMaxQuantJobs = 16;
+struct QuantJob {
+  const float* W;
+  uint8_t* codes;
+  uint8_t* scale8;
+  float* scale2;
+  int64_t n, g0;
+};
+struct QuantJobs {
+  QuantJob j[kMaxQuantJobs];
+  int count;
+};
+hipError_t launch_quantize_grouped(const QuantJobs& jobs, int32_t* flags, int fmt, hipStream_t st);
 // dq: second-level variant (0 default; 1 int8 around the tensor mean; 2 E4M3
 // around it, the mean stored after the steps in scale2).
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scale8, const float* scale2,

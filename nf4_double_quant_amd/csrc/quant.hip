@@ -76,12 +76,13 @@ __device__ __forceinline__ Rsrc rsrc(const void* base, int64_t bytes) {
                                            0x00020000);
 }
 
-__global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, int64_t n,
-                                                  uint8_t* __restrict__ codes,
-                                                  uint8_t* __restrict__ scale8,
-                                                  float* __restrict__ scale2,
-                                                  int32_t* __restrict__ flags, Codebook cb,
-                                                  EncodeGuide eg) {
+// Group g of one tensor (a workgroup of 256 threads).
+__device__ __forceinline__ void quantize_group(const float* __restrict__ W, int64_t n,
+                                               uint8_t* __restrict__ codes,
+                                               uint8_t* __restrict__ scale8,
+                                               float* __restrict__ scale2,
+                                               int32_t* __restrict__ flags, const Codebook& cb,
+                                               const EncodeGuide& eg, int64_t g) {
   __shared__ __attribute__((aligned(16))) float s_thr[kGroup][16];   // per-block thresholds
   __shared__ uint32_t s_guide[(kGuideCells + 3) / 4];
   __shared__ double s_mid[16];
@@ -90,7 +91,6 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, i
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int sub = lane & 7, row = lane >> 3;      // 8 lanes per block, 8 weights per lane
-  const int64_t g = blockIdx.x;
   const int64_t base = g * kGroupElems;
   const int64_t nb = (n + kBlock - 1) / kBlock;
   const int64_t nvalid = n - base;
@@ -241,6 +241,28 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, i
   if (b_glob < nb) scale8[b_glob] = (uint8_t)q;
   if (t == 0) scale2[g] = step;
   if (bad && flags != nullptr) flags[0] = flags[0] | 1;
+}
+
+__global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, int64_t n,
+                                                  uint8_t* __restrict__ codes,
+                                                  uint8_t* __restrict__ scale8,
+                                                  float* __restrict__ scale2,
+                                                  int32_t* __restrict__ flags, Codebook cb,
+                                                  EncodeGuide eg) {
+  quantize_group(W, n, codes, scale8, scale2, flags, cb, eg, blockIdx.x);
+}
+
+// Several tensors in one launch: workgroup i quantizes group i - g0 of the
+// last job whose first workgroup g0 is <= i.  The job is picked by a uniform
+// scan with constant indices, so the table stays in kernel-argument memory.
+__global__ __launch_bounds__(256) void k_quantize_grouped(QuantJobs jobs, int32_t* __restrict__ flags,
+                                                          Codebook cb, EncodeGuide eg) {
+  const int64_t i = blockIdx.x;
+  QuantJob j = jobs.j[0];
+#pragma unroll
+  for (int k = 1; k < kMaxQuantJobs; ++k)
+    if (k < jobs.count && i >= jobs.j[k].g0) j = jobs.j[k];
+  quantize_group(j.W, j.n, j.codes, j.scale8, j.scale2, flags, cb, eg, i - j.g0);
 }
 
 // ------------------------------------------------------------------ dequant
@@ -432,6 +454,18 @@ hipError_t launch_quantize(const float* W, int64_t n, uint8_t* codes, uint8_t* s
   if (eg.zero_cell < 0) return hipErrorInvalidValue;
   launch(k_quantize, dim3((unsigned)ng), dim3(256), 0, st, W, n, codes, scale8,
                      scale2, flags, host_codebook(fmt), eg);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_grouped(const QuantJobs& jobs, int32_t* flags, int fmt, hipStream_t st) {
+  if (jobs.count < 1 || jobs.count > kMaxQuantJobs) return hipErrorInvalidValue;
+  const QuantJob& last = jobs.j[jobs.count - 1];
+  const int64_t groups = last.g0 + (last.n + kGroupElems - 1) / kGroupElems;
+  if (groups == 0) return hipSuccess;
+  if (groups > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const EncodeGuide& eg = host_encode_guide(fmt);
+  if (eg.zero_cell < 0) return hipErrorInvalidValue;
+  launch(k_quantize_grouped, dim3((unsigned)groups), dim3(256), 0, st, jobs, flags, host_codebook(fmt), eg);
   return hipGetLastError();
 }
 

@@ -192,6 +192,25 @@ static void other_validation(void) {
   CHECK(qlora_quantize_nf4_dq(f, INT64_MAX, &vmax, NULL, NULL) == QLORA_E_SHAPE);
   CHECK(qlora_dequant(&vmax, 0, A16, NULL) == QLORA_E_SHAPE);
 
+  /* grouped quantizer */
+  {
+    const float* Wg[3] = {f, f, NULL};
+    qlora_nf4dq vg[3] = {view(128, 0, 0), view(64, 0, 0), view(0, 0, 0)};
+    CHECK(qlora_quantize_nf4_dq_grouped(Wg, vg, 0, NULL, NULL) == QLORA_OK);
+    CHECK(qlora_quantize_nf4_dq_grouped(Wg, vg, -1, NULL, NULL) == QLORA_E_INVALID);
+    CHECK(qlora_quantize_nf4_dq_grouped(Wg, vg, QLORA_MAX_GROUPED + 1, NULL, NULL) == QLORA_E_INVALID);
+    CHECK(qlora_quantize_nf4_dq_grouped(NULL, vg, 3, NULL, NULL) == QLORA_E_INVALID);
+    CHECK(qlora_quantize_nf4_dq_grouped(Wg, NULL, 3, NULL, NULL) == QLORA_E_INVALID);
+    const float* Wm[2] = {f, (const float*)MIS(4)};
+    CHECK(qlora_quantize_nf4_dq_grouped(Wm, vg, 2, NULL, NULL) == QLORA_E_ALIGN);
+    qlora_nf4dq vmix[2] = {view(128, 0, 0), view(64, 2, 0)};
+    CHECK(qlora_quantize_nf4_dq_grouped(Wg, vmix, 2, NULL, NULL) == QLORA_E_INVALID);
+    qlora_nf4dq vbig[2] = {view(128, 0, 0), view(INT64_MAX, 0, 0)};
+    CHECK(qlora_quantize_nf4_dq_grouped(Wg, vbig, 2, NULL, NULL) == QLORA_E_SHAPE);
+    qlora_nf4dq vdq[1] = {view(128, 0, 1)};          /* the default second level only */
+    CHECK(qlora_quantize_nf4_dq_grouped(Wg, vdq, 1, NULL, NULL) == QLORA_E_INVALID);
+  }
+
   /* merge */
   const qlora_bf16* b = (const qlora_bf16*)A16;
   float* out = (float*)A16;
@@ -230,6 +249,11 @@ static void no_device(void) {
   qlora_bf16* w = (qlora_bf16*)A16;
   CHECK(qlora_quantize_nf4_dq((const float*)A16, 128 * 128, &v, NULL, NULL) == QLORA_E_NO_DEVICE);
   CHECK(qlora_dequant(&v, 0, A16, NULL) == QLORA_E_NO_DEVICE);
+  {
+    const float* Wg[2] = {(const float*)A16, (const float*)A16};
+    qlora_nf4dq vg[2] = {view(128 * 128, 0, 0), view(100, 0, 0)};
+    CHECK(qlora_quantize_nf4_dq_grouped(Wg, vg, 2, NULL, NULL) == QLORA_E_NO_DEVICE);
+  }
   CHECK(fwd(&v, A16, 8, 128, 128, A16, 8, (size_t)1 << 30) == QLORA_E_NO_DEVICE);
   CHECK(qlora_linear_bwd_noalloc(b, b, NULL, 8, 128, &v, 128, b, b, 8, 2.0f, w, w, w, NULL) ==
         QLORA_E_NO_DEVICE);

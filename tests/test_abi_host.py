@@ -140,6 +140,30 @@ def test_validation_statuses(L):
                A16, 1 << 30, None) == 1                     # dA missing
 
 
+def test_grouped_quantize_validation(L):
+    f = L.qlora_quantize_nf4_dq_grouped
+    Vs = (qb._NF4DQ * 3)(_view(128), _view(64), _view(0))
+    W = (ctypes.c_void_p * 3)(A16, A16, None)               # the empty tensor needs no data
+    assert f(W, Vs, 0, None, None) == 0                      # no tensors: no-op
+    assert f(W, Vs, -1, None, None) == 1
+    assert f(W, Vs, qb.QLORA_MAX_GROUPED + 1, None, None) == 1
+    assert f(None, Vs, 3, None, None) == 1
+    assert f(W, None, 3, None, None) == 1
+    bad = (ctypes.c_void_p * 3)(A16, None, None)            # n = 64 but no data
+    assert f(bad, Vs, 3, None, None) == 1
+    mis = (ctypes.c_void_p * 3)(A16, A16 + 4, None)
+    assert f(mis, Vs, 3, None, None) == 3
+    mixed = (qb._NF4DQ * 2)(_view(128), _view(64, fmt=2))   # one table per call
+    assert f(W, mixed, 2, None, None) == 1
+    dq = (qb._NF4DQ * 1)(_view(128))
+    dq[0].dq = 1                                             # the default second level only
+    assert f(W, dq, 1, None, None) == 1
+    big = (qb._NF4DQ * 1)(_view((1 << 40) + 1))
+    assert f(W, big, 1, None, None) == 2
+    empty = (qb._NF4DQ * 2)(_view(0), _view(0))
+    assert f((ctypes.c_void_p * 2)(None, None), empty, 2, None, None) == 0   # nothing to launch
+
+
 def test_multi_adapter_validation(L):
     f = L.qlora_linear_fwd_multi
     v = _view(128 * 128)
@@ -213,6 +237,8 @@ def test_no_device_status(L):
                               A16, 1 << 30, None) == 5
     # size-0 work is a no-op even without a device
     assert L.qlora_quantize_nf4_dq(A16, 0, ctypes.byref(_view(0)), None, None) == 0
+    Vs = (qb._NF4DQ * 2)(_view(128), _view(64))
+    assert L.qlora_quantize_nf4_dq_grouped((ctypes.c_void_p * 2)(A16, A16), Vs, 2, None, None) == 5
     # the allocation-free backward: sizes that fit reach the device probe
     assert L.qlora_linear_bwd_noalloc(A16, A16, None, 8, 128, ctypes.byref(v), 128, A16, A16, 8,
                                       2.0, A16, A16, A16, None) == 5
