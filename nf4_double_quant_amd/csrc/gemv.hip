@@ -65,14 +65,25 @@ __global__ __launch_bounds__(256) void k_lora_down_small(const uint16_t* __restr
     A += (int64_t)a * d * r;
   }
   // this lane's activations for its four 32-wide k steps, requested before
-  // the adapter tile so that both arrive in one round trip
+  // the adapter tile so that both arrive in one round trip.  Every load is
+  // unconditional (offsets outside a buffer read 0): a branch around a load
+  // would make the compiler wait for all earlier loads before the next one.
+  // (32-bit offsets from descriptors based at this slice: M·d and 512·r
+  // elements are far below 2^31)
+  const int kn = (int)min<int64_t>(kPrepK, d - k0);    // valid k of the slice
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(X + k0), (short)0, (int)(((int64_t)(M - 1) * d + kn) * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(A + k0 * r), (short)0, kn * r * 2, 0x00020000);
+  constexpr uint32_t kOff = 0x7FFFFFF0u;           // an offset every descriptor rejects
+  const uint32_t d32 = (uint32_t)d;
   uint4 xv[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const int64_t kx = k0 + (w * 4 + q) * 32 + 8 * g;
-    xv[q] = make_uint4(0, 0, 0, 0);
-    if (m < M && kx < d && (only < 0 || m == only))
-      xv[q] = *reinterpret_cast<const uint4*>(X + (int64_t)m * d + kx);
+    const int kx = (w * 4 + q) * 32 + 8 * g;        // within the slice
+    const bool ok = m < M && kx < kn && (only < 0 || m == only);
+    xv[q] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                          rx, (int)(ok ? ((uint32_t)m * d32 + (uint32_t)kx) * 2u : kOff), 0, 0));
   }
   // stage A[k0:k0+512][c0:c0+64] (zeros outside); all 16 loads of a thread
   // are in flight before the first store
@@ -81,10 +92,10 @@ __global__ __launch_bounds__(256) void k_lora_down_small(const uint16_t* __restr
 #pragma unroll
     for (int u = 0; u < kPrepK * 8 / 256; ++u) {
       const int i = u * 256 + t, row = i >> 3, ch = i & 7;
-      const int64_t k = k0 + row;
       const int col = c0 + ch * 8;
-      v[u] = make_uint4(0, 0, 0, 0);
-      if (k < d && col < r) v[u] = *reinterpret_cast<const uint4*>(A + k * r + col);
+      const bool ok = row < kn && col < r;
+      v[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           ra, (int)(ok ? (uint32_t)(row * r + col) * 2u : kOff), 0, 0));
     }
 #pragma unroll
     for (int u = 0; u < kPrepK * 8 / 256; ++u) {
