@@ -6,16 +6,19 @@
 // the first-level constants, then quantize those constants).
 //
 // gfx950 design
-//  * One workgroup per double-quant group (16384 weights = 64 KB of fp32):
-//    the group's second-level constant needs every block's absmax, so the
-//    whole group is loaded at once into VGPRs (16 float4 per lane) and HBM
-//    is read exactly once.
-//  * 8 lanes per 64-weight block, 8 consecutive weights per lane.  A
-//    block's codes need only its own absmax, so only the small second level
-//    waits for the whole group: pass 1 takes each block's absmax, thresholds
-//    and cell reciprocal as its two loads land; pass 2 encodes the eight
-//    blocks of a lane two at a time (their LDS reads in flight together)
-//    and stores them.
+//  * One workgroup of 8 waves per double-quant group (16384 weights = 64 KB
+//    of fp32): the group's second-level constant needs every block's
+//    absmax, so the whole group is loaded at once into VGPRs (8 float4 per
+//    lane) and HBM is read exactly once.  Eight waves per group (rather than
+//    four with twice the weights per lane) halve each group's encode time
+//    and leave two groups per CU in flight, which streams large tensors
+//    from HBM faster than more, slower groups per CU.
+//  * 8 lanes per 64-weight block, 8 consecutive weights per lane, 4 blocks
+//    per lane.  A block's codes need only its own absmax, so only the small
+//    second level waits for the whole group: pass 1 takes each block's
+//    absmax, thresholds and cell reciprocal as its two loads land; pass 2
+//    encodes the four blocks of a lane two at a time (their LDS reads in
+//    flight together) and stores them.
 //  * The block absmax is an 8-lane DPP max on the integer bits of |w|
 //    (integer order equals float order for non-negative floats, and NaN/Inf
 //    land above every finite value, which is how non-finite input is
@@ -76,7 +79,10 @@ __device__ __forceinline__ Rsrc rsrc(const void* base, int64_t bytes) {
                                            0x00020000);
 }
 
-// Group g of one tensor (a workgroup of 256 threads).
+constexpr int kQuantWaves = 8;                                   // waves per group
+constexpr int kLaneBlocks = kGroup / (kQuantWaves * 8);        // blocks per lane: 4
+
+// Group g of one tensor (a workgroup of 64·kQuantWaves threads).
 __device__ __forceinline__ void quantize_group(const float* __restrict__ W, int64_t n,
                                                uint8_t* __restrict__ codes,
                                                uint8_t* __restrict__ scale8,
@@ -87,7 +93,7 @@ __device__ __forceinline__ void quantize_group(const float* __restrict__ W, int6
   __shared__ uint32_t s_guide[(kGuideCells + 3) / 4];
   __shared__ double s_mid[16];
   __shared__ uint32_t s_c1[kGroup];
-  __shared__ uint32_t s_red[4];
+  __shared__ uint32_t s_red[kQuantWaves];
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int sub = lane & 7, row = lane >> 3;      // 8 lanes per block, 8 weights per lane
@@ -97,10 +103,10 @@ __device__ __forceinline__ void quantize_group(const float* __restrict__ W, int6
 
   // ---- issue every load of the group (reads past n return 0)
   const Rsrc rw = rsrc(W + base, (min((int64_t)kGroupElems, nvalid)) * 4);
-  float4 v[16];
+  float4 v[2 * kLaneBlocks];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int bl = wave * 64 + j * 8 + row;
+  for (int j = 0; j < kLaneBlocks; ++j) {
+    const int bl = (wave * kLaneBlocks + j) * 8 + row;
     const int off = (bl * kBlock + sub * 8) * 4;
     v[2 * j] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 0));
     v[2 * j + 1] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rw, off + 16, 0, 0));
@@ -124,10 +130,10 @@ __device__ __forceinline__ void quantize_group(const float* __restrict__ W, int6
   // ---- pass 1, per block as its loads land: absmax, thresholds and the
   // factors of the cell computation
   uint32_t bad = 0, tiny_any = 0;
-  float inv[8];
+  float inv[kLaneBlocks];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int bl = wave * 64 + j * 8 + row;
+  for (int j = 0; j < kLaneBlocks; ++j) {
+    const int bl = (wave * kLaneBlocks + j) * 8 + row;
     const float4 p = v[2 * j], q = v[2 * j + 1];
     uint32_t a = max(max(max(abs_bits(p.x), abs_bits(p.y)), max(abs_bits(p.z), abs_bits(p.w))),
                      max(max(abs_bits(q.x), abs_bits(q.y)), max(abs_bits(q.z), abs_bits(q.w))));
@@ -152,12 +158,12 @@ __device__ __forceinline__ void quantize_group(const float* __restrict__ W, int6
 
   // ---- pass 2: encode and store.  The cell of x = w/c1 gives a guide code
   // that is the code of w or one below it, and one threshold compare decides.
-  // Straight-line over the eight blocks unless a block is tiny or the group
+  // Straight-line over the lane's blocks unless a block is tiny or the group
   // ends inside a code word.
   auto encode_store = [&](auto generic) {
     constexpr bool kGeneric = decltype(generic)::value;
 #pragma unroll
-    for (int jp = 0; jp < 8; jp += 2) {                // two blocks at a time
+    for (int jp = 0; jp < kLaneBlocks; jp += 2) {                // two blocks at a time
       uint32_t cell[16], g0[16], k[16];
       float th[16];
 #pragma unroll
@@ -166,7 +172,7 @@ __device__ __forceinline__ void quantize_group(const float* __restrict__ W, int6
         const float4 p = v[2 * j], q = v[2 * j + 1];
         const float w[8] = {p.x, p.y, p.z, p.w, q.x, q.y, q.z, q.w};
         float sc = 1.0f;
-        if constexpr (kGeneric) sc = s_c1[wave * 64 + j * 8 + row] - 1u < 0x0D800000u - 1u ? 0x1p64f : 1.0f;
+        if constexpr (kGeneric) sc = s_c1[(wave * kLaneBlocks + j) * 8 + row] - 1u < 0x0D800000u - 1u ? 0x1p64f : 1.0f;
         // inv = 0 marks an all-zero or non-finite block
         const float c0 = inv[j] != 0.0f ? cell_base : zero_base;
 #pragma unroll
@@ -179,7 +185,7 @@ __device__ __forceinline__ void quantize_group(const float* __restrict__ W, int6
 #pragma unroll
       for (int e = 0; e < 16; ++e) g0[e] = guide[cell[e]];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) th[e] = s_thr[wave * 64 + (jp + (e >> 3)) * 8 + row][g0[e]];
+      for (int e = 0; e < 16; ++e) th[e] = s_thr[(wave * kLaneBlocks + jp + (e >> 3)) * 8 + row][g0[e]];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int j = jp + h;
@@ -191,7 +197,7 @@ __device__ __forceinline__ void quantize_group(const float* __restrict__ W, int6
         // word `sub` of the block: byte e = code e | code e+4 << 4
         uint32_t word = (kk[0] | (kk[4] << 4)) | ((kk[1] | (kk[5] << 4)) << 8) |
                         ((kk[2] | (kk[6] << 4)) << 16) | ((kk[3] | (kk[7] << 4)) << 24);
-        const int wi = (wave * 64 + j * 8 + row) * 8 + sub;     // word within the group
+        const int wi = ((wave * kLaneBlocks + j) * 8 + row) * 8 + sub;     // word within the group
         if constexpr (kGeneric) {
           // The word holding code n-1 may end in codes past n; they are
           // stored as 7, the layout's padding, whatever a zero weight
@@ -214,14 +220,16 @@ __device__ __forceinline__ void quantize_group(const float* __restrict__ W, int6
     encode_store(std::false_type{});
   __syncthreads();
 
-  // ---- second level: one thread per block
-  const uint32_t c1_bits = s_c1[t];
+  // ---- second level: one thread per block (threads 0..255)
+  const uint32_t c1_bits = t < kGroup ? s_c1[t] : 0u;
   uint32_t m = c1_bits;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
   if (lane == 0) s_red[wave] = m;
   __syncthreads();
-  m = max(max(s_red[0], s_red[1]), max(s_red[2], s_red[3]));
+  m = s_red[0];
+#pragma unroll
+  for (int i = 1; i < kQuantWaves; ++i) m = max(m, s_red[i]);
   const float c1 = __uint_as_float(c1_bits);
   const float c2 = __uint_as_float(m);
   // fp64 quotient of fp32 operands rounded to fp32 is the correctly rounded quotient.
@@ -238,12 +246,12 @@ __device__ __forceinline__ void quantize_group(const float* __restrict__ W, int6
     q = min(q, 255u);
   }
   const int64_t b_glob = g * kGroup + t;
-  if (b_glob < nb) scale8[b_glob] = (uint8_t)q;
+  if (t < kGroup && b_glob < nb) scale8[b_glob] = (uint8_t)q;
   if (t == 0) scale2[g] = step;
   if (bad && flags != nullptr) flags[0] = flags[0] | 1;
 }
 
-__global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, int64_t n,
+__global__ __launch_bounds__(64 * kQuantWaves) void k_quantize(const float* __restrict__ W, int64_t n,
                                                   uint8_t* __restrict__ codes,
                                                   uint8_t* __restrict__ scale8,
                                                   float* __restrict__ scale2,
@@ -255,7 +263,7 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, i
 // Several tensors in one launch: workgroup i quantizes group i - g0 of the
 // last job whose first workgroup g0 is <= i.  The job is picked by a uniform
 // scan with constant indices, so the table stays in kernel-argument memory.
-__global__ __launch_bounds__(256) void k_quantize_grouped(QuantJobs jobs, int32_t* __restrict__ flags,
+__global__ __launch_bounds__(64 * kQuantWaves) void k_quantize_grouped(QuantJobs jobs, int32_t* __restrict__ flags,
                                                           Codebook cb, EncodeGuide eg) {
   const int64_t i = blockIdx.x;
   QuantJob j = jobs.j[0];
@@ -452,7 +460,7 @@ hipError_t launch_quantize(const float* W, int64_t n, uint8_t* codes, uint8_t* s
   if (ng == 0) return hipSuccess;
   const EncodeGuide& eg = host_encode_guide(fmt);
   if (eg.zero_cell < 0) return hipErrorInvalidValue;
-  launch(k_quantize, dim3((unsigned)ng), dim3(256), 0, st, W, n, codes, scale8,
+  launch(k_quantize, dim3((unsigned)ng), dim3(64 * kQuantWaves), 0, st, W, n, codes, scale8,
                      scale2, flags, host_codebook(fmt), eg);
   return hipGetLastError();
 }
@@ -465,7 +473,7 @@ hipError_t launch_quantize_grouped(const QuantJobs& jobs, int32_t* flags, int fm
   if (groups > 0x7FFFFFFF) return hipErrorInvalidValue;
   const EncodeGuide& eg = host_encode_guide(fmt);
   if (eg.zero_cell < 0) return hipErrorInvalidValue;
-  launch(k_quantize_grouped, dim3((unsigned)groups), dim3(256), 0, st, jobs, flags, host_codebook(fmt), eg);
+  launch(k_quantize_grouped, dim3((unsigned)groups), dim3(64 * kQuantWaves), 0, st, jobs, flags, host_codebook(fmt), eg);
   return hipGetLastError();
 }
 
