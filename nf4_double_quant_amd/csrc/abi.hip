@@ -533,15 +533,19 @@ int qlora_linear_bwd(const qlora_bf16* dY, const qlora_bf16* X, const float* T, 
     QL_RUN(QLORA_K_GRADS, hs,
            launch_rank_grads(RankGradJob{X, d, sU, dApart, true, 0},
                              RankGradJob{dY, o, sT, dBpart, false, 0}, (int)r, M, hs));
-    QL_RUN(QLORA_K_GRADS, hs,
-           launch_reduce_planes(ReduceJob{dApart, (int)L.g_splits, d * r, d * r, nullptr, dA, 1.0f},
-                                ReduceJob{dBpart, (int)L.g_splits, r * o, r * o, nullptr, dB, 1.0f},
-                                hs));
   }
+  // the sums of the dA and dB planes: at the end of the dX launch when there
+  // is one (a launch fewer), else on their own
+  const ReduceJob sum_dA = r > 0 ? ReduceJob{dApart, (int)L.g_splits, d * r, d * r, nullptr, dA, 1.0f}
+                                 : ReduceJob{};
+  const ReduceJob sum_dB = r > 0 ? ReduceJob{dBpart, (int)L.g_splits, r * o, r * o, nullptr, dB, 1.0f}
+                                 : ReduceJob{};
   if (dX != nullptr) {
     QL_RUN(QLORA_K_MAIN_GEMM, hs,
            launch_qgemm(true, dY, o, W->codes, W->scale8, W->scale2, d, sU, r, A, r, M, d, o,
-                        lora ? r : 0, dX, d, host_codebook(W->fmt), hs));
+                        lora ? r : 0, dX, d, host_codebook(W->fmt), hs, sum_dA, sum_dB));
+  } else if (r > 0) {
+    QL_RUN(QLORA_K_GRADS, hs, launch_reduce_planes(sum_dA, sum_dB, hs));
   }
   return QLORA_OK;
 }

@@ -12,32 +12,9 @@ __global__ __launch_bounds__(256) void k_reduce_planes(ReduceJob a, ReduceJob b,
   const ReduceJob& jo = first ? a : b;
   const int64_t blk = first ? blockIdx.x : blockIdx.x - blocks_a;
   const int64_t nblk = first ? blocks_a : gridDim.x - blocks_a;
-  const float* part = jo.part;
-  const int splits = jo.splits;
-  const int64_t plane = jo.plane, n4 = jo.count / 4;
-  for (int64_t i = blk * blockDim.x + threadIdx.x; i < n4; i += nblk * blockDim.x) {
-    // planes summed in order, four loads in flight at a time
-    float4 s = reinterpret_cast<const float4*>(part)[i];
-    int z = 1;
-    for (; z + 4 <= splits; z += 4) {
-      float4 v[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = reinterpret_cast<const float4*>(part + (int64_t)(z + u) * plane)[i];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) { s.x += v[u].x; s.y += v[u].y; s.z += v[u].z; s.w += v[u].w; }
-    }
-    for (; z < splits; ++z) {
-      const float4 v = reinterpret_cast<const float4*>(part + (int64_t)z * plane)[i];
-      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
-    }
-    if (jo.out_f32) reinterpret_cast<float4*>(jo.out_f32)[i] = s;
-    if (jo.out_bf16) {
-      uint2 o;
-      o.x = pack_bf16x2(jo.scale * s.x, jo.scale * s.y);
-      o.y = pack_bf16x2(jo.scale * s.z, jo.scale * s.w);
-      reinterpret_cast<uint2*>(jo.out_bf16)[i] = o;
-    }
-  }
+  const int64_t n4 = jo.count / 4;
+  for (int64_t i = blk * blockDim.x + threadIdx.x; i < n4; i += nblk * blockDim.x)
+    reduce_planes_quad(jo, i);
 }
 
 __global__ __launch_bounds__(256) void k_fill_zero_bf16(uint16_t* __restrict__ y, int64_t n) {

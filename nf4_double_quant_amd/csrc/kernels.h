@@ -62,14 +62,67 @@ hipError_t launch_dq_variant(const float* W, int64_t n, uint8_t* scale8, float* 
                              double* psum, hipStream_t st);
 
 
+// Contiguous split planes [splits][count] (count % 4 == 0) -> their sum, in
+// plane order: out_f32 = Σ, out_bf16 = bf16(scale·Σ).  With one plane it is
+// the conversion to bf16(scale·x).  Two independent jobs per launch (the
+// second may have count 0).
+struct ReduceJob {
+  const float* part;
+  int splits;
+  int64_t plane, count;
+  float* out_f32;
+  uint16_t* out_bf16;
+  float scale;
+};
+hipError_t launch_reduce_planes(const ReduceJob& a, const ReduceJob& b, hipStream_t st);
+
+// Element quad i (of count/4) of a plane sum: the planes are added in order,
+// up to eight loads in flight.
+__device__ __forceinline__ void reduce_planes_quad(const ReduceJob& jo, int64_t i) {
+  const float4* part = reinterpret_cast<const float4*>(jo.part);
+  const int64_t pl = jo.plane / 4;
+  const int nb = jo.splits < 8 ? jo.splits : 8;      // the first batch, plane 0 included
+  float4 v0[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u)
+    if (u < nb) v0[u] = part[(int64_t)u * pl + i];
+  float4 s = v0[0];
+#pragma unroll
+  for (int u = 1; u < 8; ++u)
+    if (u < nb) { s.x += v0[u].x; s.y += v0[u].y; s.z += v0[u].z; s.w += v0[u].w; }
+  int z = nb;
+  for (; z + 8 <= jo.splits; z += 8) {
+    float4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = part[(int64_t)(z + u) * pl + i];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) { s.x += v[u].x; s.y += v[u].y; s.z += v[u].z; s.w += v[u].w; }
+  }
+  for (; z < jo.splits; ++z) {
+    const float4 v = part[(int64_t)z * pl + i];
+    s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+  }
+  if (jo.out_f32) reinterpret_cast<float4*>(jo.out_f32)[i] = s;
+  if (jo.out_bf16) {
+    uint2 o;
+    o.x = pack_bf16x2(jo.scale * s.x, jo.scale * s.y);
+    o.y = pack_bf16x2(jo.scale * s.z, jo.scale * s.w);
+    reinterpret_cast<uint2*>(jo.out_bf16)[i] = o;
+  }
+}
+
 // Fused NF4 dequant-GEMM: C = A·Ŵ (+ A2·B2) with Ŵ from the quantized Wq[o][d].
 // trans_w = false: forward, C[M][N=o] = A[M][K=d]·Wqᵀ + A2·B2, B2 = B [K2][N].
 // trans_w = true:  backward, C[M][N=d] = A[M][K=o]·Wq + A2·B2ᵀ, B2 = A [N][K2].
+// tail_a/tail_b: plane sums (as launch_reduce_planes) that the same launch
+// performs after its tiles, their planes complete before it starts; jobs
+// with count 0 are skipped.
 hipError_t launch_qgemm(bool trans_w, const uint16_t* A, int64_t lda, const uint8_t* codes,
                         const uint8_t* scale8, const float* scale2, int64_t d,
                         const uint16_t* A2, int64_t lda2, const uint16_t* B2, int64_t ldb2,
                         int64_t M, int64_t N, int64_t K, int64_t K2, uint16_t* C, int64_t ldc,
-                        const Codebook& cb, hipStream_t st);
+                        const Codebook& cb, hipStream_t st, const ReduceJob& tail_a = ReduceJob{},
+                        const ReduceJob& tail_b = ReduceJob{});
 
 // Rank-r products (split planes, summed by launch_reduce_planes):
 // part[z][M][r] = P[M][K-slice z]·Q with Q = Qsrc[K][r], or Q = Qsrc[r][K]ᵀ
@@ -92,19 +145,6 @@ struct RankGradJob {
 int rank_grad_splits(int64_t M);
 hipError_t launch_rank_grads(RankGradJob a, RankGradJob b, int r, int64_t M, hipStream_t st);
 
-// Contiguous split planes [splits][count] (count % 4 == 0) -> their sum, in
-// plane order: out_f32 = Σ, out_bf16 = bf16(scale·Σ).  With one plane it is
-// the conversion to bf16(scale·x).  Two independent jobs per launch (the
-// second may have count 0).
-struct ReduceJob {
-  const float* part;
-  int splits;
-  int64_t plane, count;
-  float* out_f32;
-  uint16_t* out_bf16;
-  float scale;
-};
-hipError_t launch_reduce_planes(const ReduceJob& a, const ReduceJob& b, hipStream_t st);
 hipError_t launch_fill_zero_bf16(uint16_t* y, int64_t n, hipStream_t st);
 
 // Few-token forward (M <= kGemvMaxTokens): Tpart [gemv_tsplits(d)][M][r]

@@ -34,6 +34,8 @@
 // works on a contiguous band of output tiles.
 #include <type_traits>
 
+#include <stddef.h>
+
 #include "kernels.h"
 
 namespace qlora {
@@ -116,6 +118,7 @@ struct QGemmArgs {
   int64_t M, N, K, K2;
   uint16_t* C; int64_t ldc;
   Codebook cb;
+  ReduceJob tail_a, tail_b;          // plane sums done after the tiles (count 0: none)
 };
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -491,16 +494,45 @@ __global__ __launch_bounds__(64 * kWaves) void k_qgemm(QGemmArgs p) {
     const uint32_t off = col < p.N ? (uint32_t)((row * p.ldc + col) * 2) : kOobOff;
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), rcout, (int)off, 0, 0);
   }
+
+  // ---- plane sums handed to this launch (their planes were written by an
+  // earlier launch): every workgroup takes a strided share of the quads.
+  // The jobs are read from the kernel arguments only here, through a pointer
+  // the compiler cannot see through, so they are not loaded at entry and
+  // held in (spilled) scalar registers across the main loop.
+  typedef const __attribute__((address_space(4))) char KChar;
+  KChar* ka = (KChar*)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(ka));
+  typedef const __attribute__((address_space(4))) ReduceJob KJob;
+  const KJob* tails = reinterpret_cast<const KJob*>(ka + offsetof(QGemmArgs, tail_a));
+  static_assert(offsetof(QGemmArgs, tail_b) == offsetof(QGemmArgs, tail_a) + sizeof(ReduceJob),
+                "the two jobs are adjacent");
+  const int64_t tstride = (int64_t)gridDim.x * kT;
+#pragma unroll 1
+  for (int u = 0; u < 2; ++u) {
+    ReduceJob job;
+    job.part = tails[u].part;
+    job.splits = tails[u].splits;
+    job.plane = tails[u].plane;
+    job.count = tails[u].count;
+    job.out_f32 = tails[u].out_f32;
+    job.out_bf16 = tails[u].out_bf16;
+    job.scale = tails[u].scale;
+    for (int64_t i = (int64_t)blockIdx.x * kT + t; i < job.count / 4; i += tstride)
+      reduce_planes_quad(job, i);
+  }
 }
 
 hipError_t launch_qgemm(bool trans_w, const uint16_t* A, int64_t lda, const uint8_t* codes,
                         const uint8_t* scale8, const float* scale2, int64_t d,
                         const uint16_t* A2, int64_t lda2, const uint16_t* B2, int64_t ldb2,
                         int64_t M, int64_t N, int64_t K, int64_t K2, uint16_t* C, int64_t ldc,
-                        const Codebook& cb, hipStream_t st) {
-  if (M == 0 || N == 0) return hipSuccess;
+                        const Codebook& cb, hipStream_t st, const ReduceJob& tail_a,
+                        const ReduceJob& tail_b) {
+  if (M == 0 || N == 0)   // no tiles: the plane sums run on their own
+    return tail_a.count + tail_b.count > 0 ? launch_reduce_planes(tail_a, tail_b, st) : hipSuccess;
   QGemmArgs p{A, lda, codes, scale8, scale2, d, A2, lda2, B2, ldb2, M, N, K, K2, C, ldc,
-              cb};
+              cb, tail_a, tail_b};
   const unsigned tiles = (unsigned)(((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN));
   if (trans_w)
     launch(k_qgemm<true, kWaves>, dim3(tiles), dim3(64 * kWaves), 0, st, p);

@@ -13,8 +13,9 @@
 //    dA and dB in one launch; both operands are token-major, streamed into
 //    LDS as [m][·] rows and gathered with ds_read_b64_tr_b16 (4 consecutive
 //    tokens of one column per read).
-// Split planes are summed in a fixed order by k_reduce_planes, so results
-// are bitwise reproducible.  (Summing them inside these kernels, with the
+// Split planes are summed in a fixed order (k_reduce_planes, or the tail of
+// the backward dX launch for the dA and dB planes), so results are bitwise
+// reproducible.  (Summing them inside these kernels, with the
 // last workgroup of a tile reducing, costs more on this chip: every
 // device-scope release fence writes back the XCD's whole L2.)
 #include <type_traits>
