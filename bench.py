@@ -42,7 +42,7 @@ MFMA_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES", "GRBM_GUI_ACTI
 # grid size that selects its dispatches of that workload (None: all).
 PMC_KERNELS = {
     "k_qgemm": ("k_qgemm", ["qgemm.hip", "common.h"], "linear_4096", None),
-    "k_quantize": ("k_quantize", ["quant.hip", "common.h"], "linear_4096", 1024 * 256),
+    "k_quantize": ("k_quantize", ["quant.hip", "common.h"], "linear_4096", 1024 * 512),   # 1024 groups × 512 threads
     "k_rank_down": ("k_rank_down", ["rank.hip", "common.h"], "linear_4096", None),
     "k_rank_grad": ("k_rank_grad", ["rank.hip", "common.h"], "linear_4096", None),
     "k_reduce_planes": ("k_reduce_planes", ["gemm.hip", "common.h"], "linear_4096", None),
