@@ -117,6 +117,12 @@ def test_no_dx_and_zero_tokens():
     W, X, A, B, dY = make_case(16, 128, 64, 8, seed=4)
     Y, T, dX, dA, dB = run_gpu(W, X, A, B, dY, 2.0, need_dX=False)
     assert dX is None and dA is not None
+    # without dX the adapter-gradient planes are summed by their own launch,
+    # with dX at the end of the dX GEMM: same order, same bits
+    _, _, dX2, dA2, dB2 = run_gpu(W, X, A, B, dY, 2.0)
+    assert dX2 is not None
+    assert torch.equal(dA.view(torch.int16), dA2.view(torch.int16))
+    assert torch.equal(dB.view(torch.int16), dB2.view(torch.int16))
     q = qb.qlora_quantize_nf4_dq(torch.from_numpy(W).cuda())
     Xe = torch.empty((0, 128), dtype=torch.bfloat16, device="cuda")
     Ye, Te = qb.qlora_linear_fwd(Xe, q, bf16_dev(A), bf16_dev(B), 2.0)
