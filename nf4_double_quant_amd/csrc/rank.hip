@@ -211,7 +211,7 @@ __global__ __launch_bounds__(256) void k_rank_down(const uint16_t* __restrict__ 
 
 namespace {
 constexpr int kGradP = 128;       // big-dimension columns per workgroup (4 waves × 32)
-constexpr int kGradM = 512;       // tokens per workgroup (split of the reduction)
+constexpr int kGradM = 1024;      // tokens per workgroup (split of the reduction)
 constexpr int kGradChunk = 64;    // tokens per LDS stage
 constexpr int kBigStage = kGradChunk * kGradP;   // bf16 elements of a BIG stage (16 KB)
 constexpr int kSmallStage = kGradChunk * 64;     // bf16 elements of a SMALL stage (8 KB)
@@ -342,7 +342,7 @@ __global__ __launch_bounds__(256) void k_rank_grad(RankGradJob ja, RankGradJob j
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  constexpr int kChunks = kGradM / kGradChunk;   // a slice shorter than 512 streams zero stages
+  constexpr int kChunks = kGradM / kGradChunk;   // a slice shorter than kGradM streams zero stages
   const uint32_t ob0 = frag_off<true>(w * 32, lane), ob1 = frag_off<true>(w * 32 + 16, lane);
   const uint32_t os0 = frag_off<false>(0, lane), os1 = frag_off<false>(16, lane);
   const uint32_t os2 = frag_off<false>(32, lane), os3 = frag_off<false>(48, lane);
