@@ -251,7 +251,9 @@ __device__ __forceinline__ void quantize_group(const float* __restrict__ W, int6
   if (bad && flags != nullptr) flags[0] = flags[0] | 1;
 }
 
-__global__ __launch_bounds__(64 * kQuantWaves) void k_quantize(const float* __restrict__ W, int64_t n,
+// kWavesPerSimd: the occupancy the registers are fitted to (see the launchers)
+template <int kWavesPerSimd>
+__global__ __launch_bounds__(64 * kQuantWaves) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd))) void k_quantize(const float* __restrict__ W, int64_t n,
                                                   uint8_t* __restrict__ codes,
                                                   uint8_t* __restrict__ scale8,
                                                   float* __restrict__ scale2,
@@ -263,7 +265,8 @@ __global__ __launch_bounds__(64 * kQuantWaves) void k_quantize(const float* __re
 // Several tensors in one launch: workgroup i quantizes group i - g0 of the
 // last job whose first workgroup g0 is <= i.  The job is picked by a uniform
 // scan with constant indices, so the table stays in kernel-argument memory.
-__global__ __launch_bounds__(64 * kQuantWaves) void k_quantize_grouped(QuantJobs jobs, int32_t* __restrict__ flags,
+template <int kWavesPerSimd>
+__global__ __launch_bounds__(64 * kQuantWaves) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd))) void k_quantize_grouped(QuantJobs jobs, int32_t* __restrict__ flags,
                                                           Codebook cb, EncodeGuide eg) {
   const int64_t i = blockIdx.x;
   QuantJob j = jobs.j[0];
@@ -454,14 +457,28 @@ hipError_t launch_dq_variant(const float* W, int64_t n, uint8_t* scale8, float* 
 }
 
 // ------------------------------------------------------------------ launchers
+// Workgroups per CU.  While the fp32 input stays in the 256 MB MALL the
+// quantizer runs three groups per CU (registers fitted to six waves per
+// SIMD: 80 VGPRs); a launch that streams more than kQuantStreamBytes from
+// HBM runs two (five waves per SIMD: 85 VGPRs), whose fewer, longer bursts
+// stream better.  Measured on one box against two per CU: 4096² 1–9 %
+// faster, 11008×4096 4–5 %, 8192² (268 MB) 1 %; with three per CU
+// 12288×8192 was 7 % and 22016×8192 9 % slower.
+constexpr int64_t kQuantStreamBytes = 320ll << 20;
+static bool quant_streams(int64_t groups) { return groups * (int64_t)kGroupElems * 4 > kQuantStreamBytes; }
+
 hipError_t launch_quantize(const float* W, int64_t n, uint8_t* codes, uint8_t* scale8,
                            float* scale2, int32_t* flags, int fmt, hipStream_t st) {
   const int64_t ng = (n + kGroupElems - 1) / kGroupElems;
   if (ng == 0) return hipSuccess;
   const EncodeGuide& eg = host_encode_guide(fmt);
   if (eg.zero_cell < 0) return hipErrorInvalidValue;
-  launch(k_quantize, dim3((unsigned)ng), dim3(64 * kQuantWaves), 0, st, W, n, codes, scale8,
-                     scale2, flags, host_codebook(fmt), eg);
+  if (quant_streams(ng))
+    launch(k_quantize<5>, dim3((unsigned)ng), dim3(64 * kQuantWaves), 0, st, W, n, codes, scale8, scale2,
+           flags, host_codebook(fmt), eg);
+  else
+    launch(k_quantize<6>, dim3((unsigned)ng), dim3(64 * kQuantWaves), 0, st, W, n, codes, scale8, scale2,
+           flags, host_codebook(fmt), eg);
   return hipGetLastError();
 }
 
@@ -473,7 +490,12 @@ hipError_t launch_quantize_grouped(const QuantJobs& jobs, int32_t* flags, int fm
   if (groups > 0x7FFFFFFF) return hipErrorInvalidValue;
   const EncodeGuide& eg = host_encode_guide(fmt);
   if (eg.zero_cell < 0) return hipErrorInvalidValue;
-  launch(k_quantize_grouped, dim3((unsigned)groups), dim3(64 * kQuantWaves), 0, st, jobs, flags, host_codebook(fmt), eg);
+  if (quant_streams(groups))
+    launch(k_quantize_grouped<5>, dim3((unsigned)groups), dim3(64 * kQuantWaves), 0, st, jobs, flags,
+           host_codebook(fmt), eg);
+  else
+    launch(k_quantize_grouped<6>, dim3((unsigned)groups), dim3(64 * kQuantWaves), 0, st, jobs, flags,
+           host_codebook(fmt), eg);
   return hipGetLastError();
 }
 
