@@ -56,11 +56,11 @@ __device__ __forceinline__ uint4 bload16(Rsrc r, uint32_t off) {
 }
 constexpr uint32_t kOob = 0x7FFFFFF0u;   // an offset every descriptor rejects
 
-constexpr int kDownRows = 128;    // rows of P per workgroup (4 waves × 32)
+constexpr int kDownRows = 128;    // rows of P per workgroup (8 waves × 16)
 constexpr int kDownK = 512;       // k-slice per workgroup
 constexpr int kDownLd = 80;       // LDS row stride (bf16) of the [k][j] Q tile: 64 + 16 pad
 constexpr int kDownKLd = kDownK + 8;   // LDS row stride (bf16) of the [j][k] Q tile
-constexpr int kWaveStage = 32 * 64;    // one wave's 32 rows × 64 k of P (4 KB)
+constexpr int kWaveStage = 16 * 64;    // one wave's 16 rows × 64 k of P (2 KB)
 
 // s_waitcnt vmcnt(N) (N < 64: low 4 bits in [3:0], high 2 in [15:14]),
 // other counters not waited on
@@ -80,20 +80,22 @@ __device__ __forceinline__ int pswz(int row) { return (row >> 1) & 7; }
 // kQRowMajorK: Q(k, j) = Bsrc[j][k] (K-major rows of length K); otherwise
 // Q(k, j) = Asrc[k][j] (row length r).
 //
-// P streams memory -> LDS by buffer_load ... lds: each wave owns 32 rows and
-// moves them in 64-k stages (8 rows × 128 B per instruction, whole cache
-// lines) through a 4-slot ring of its own, so the only waits are the wave's
-// own vmcnt; 16-byte chunks are XOR-swizzled by (row / 2) % 8 so the A
-// fragments (16 rows × 16 B per read) hit every bank once.
+// P streams memory -> LDS by buffer_load ... lds: each of the 8 waves owns
+// 16 rows (two waves per SIMD, since the adapter tile leaves room for one
+// workgroup per CU) and moves them in 64-k stages (8 rows × 128 B per
+// instruction, whole cache lines) through a 4-slot ring of its own, so the
+// only waits are the wave's own vmcnt; 16-byte chunks are XOR-swizzled by
+// (row / 2) % 8 so the A fragments (16 rows × 16 B per read) hit every bank
+// once.
 template <bool kQRowMajorK>
-__global__ __launch_bounds__(256) void k_rank_down(const uint16_t* __restrict__ P, int64_t M,
+__global__ __launch_bounds__(512) void k_rank_down(const uint16_t* __restrict__ P, int64_t M,
                                                    int64_t K, const uint16_t* __restrict__ Q,
                                                    int r, float* __restrict__ part) {
   __shared__ __attribute__((aligned(16))) uint16_t s_q[kQRowMajorK ? 64 * kDownKLd : kDownK * kDownLd];
   // ring slots in separate arrays: the compiler can tell a slot being read
   // from the slots the DMA is filling
-  __shared__ __attribute__((aligned(16))) uint16_t s_p0[4 * kWaveStage], s_p1[4 * kWaveStage],
-      s_p2[4 * kWaveStage], s_p3[4 * kWaveStage];
+  __shared__ __attribute__((aligned(16))) uint16_t s_p0[8 * kWaveStage], s_p1[8 * kWaveStage],
+      s_p2[8 * kWaveStage], s_p3[8 * kWaveStage];
   const int t = threadIdx.x, lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int64_t m0 = (int64_t)blockIdx.x * kDownRows;
@@ -103,14 +105,14 @@ __global__ __launch_bounds__(256) void k_rank_down(const uint16_t* __restrict__ 
   const int64_t mrows = min((int64_t)kDownRows, M - m0);
 
   // ---- Q tile loads (registers), issued first
-  constexpr int kQLoads = kQRowMajorK ? 64 * kDownK / 8 / 256 : kDownK * 8 / 256;
+  constexpr int kQLoads = kQRowMajorK ? 64 * kDownK / 8 / 512 : kDownK * 8 / 512;
   uint4 vq[kQLoads];
   if (!kQRowMajorK) {
     // Q[k0:k0+512][c0:c0+64]; rows past K and columns past r read 0
     const Rsrc rq = rsrc(Q + k0 * r, kn * r * 2);
 #pragma unroll
     for (int u = 0; u < kQLoads; ++u) {
-      const int i = u * 256 + t, row = i >> 3, col = c0 + (i & 7) * 8;
+      const int i = u * 512 + t, row = i >> 3, col = c0 + (i & 7) * 8;
       vq[u] = bload16(rq, col < r ? (uint32_t)((row * r + col) * 2) : kOob);
     }
   } else {
@@ -118,7 +120,7 @@ __global__ __launch_bounds__(256) void k_rank_down(const uint16_t* __restrict__ 
     const Rsrc rq = rsrc(Q + k0, ((int64_t)(r - 1) * K + kn) * 2);
 #pragma unroll
     for (int u = 0; u < kQLoads; ++u) {
-      const int i = u * 256 + t, row = i >> 6, ch = i & 63;     // 64 rows × 64 chunks
+      const int i = u * 512 + t, row = i >> 6, ch = i & 63;     // 64 rows × 64 chunks
       const int j = c0 + row, kk = ch * 8;
       vq[u] = bload16(rq, (j < r && kk < kn) ? (uint32_t)(((int64_t)j * K + kk) * 2) : kOob);
     }
@@ -134,8 +136,8 @@ __global__ __launch_bounds__(256) void k_rank_down(const uint16_t* __restrict__ 
   auto dma = [&](int st) {
     uint16_t* dst = slot(st);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int row = w * 32 + q * 8 + (lane >> 3);
+    for (int q = 0; q < 2; ++q) {
+      const int row = w * 16 + q * 8 + (lane >> 3);
       const int kk = st * 64 + (((lane & 7) ^ pswz(row)) << 3);
       const uint32_t off = (row < mrows && kk < kn) ? (uint32_t)((row * K + kk) * 2) : kOob;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -148,7 +150,7 @@ __global__ __launch_bounds__(256) void k_rank_down(const uint16_t* __restrict__ 
   // ---- Q tile to LDS once its loads are in (the P stages stay in flight)
 #pragma unroll
   for (int u = 0; u < kQLoads; ++u) {
-    const int i = u * 256 + t;
+    const int i = u * 512 + t;
     if (!kQRowMajorK)
       *reinterpret_cast<uint4*>(s_q + (i >> 3) * kDownLd + (i & 7) * 8) = vq[u];
     else   // row stride 1040 bytes: the 16 rows one ds_read_b128 touches fall in different banks
@@ -158,35 +160,28 @@ __global__ __launch_bounds__(256) void k_rank_down(const uint16_t* __restrict__ 
   // for them, since they write LDS)
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
-  f32x4 acc[2][4];
+  f32x4 acc[4];                          // the wave's 16 rows × 4 blocks of 16 columns
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
   const int g = lane >> 4, l16 = lane & 15;
-  const int sw = pswz(l16);              // = pswz of rows w*32 + 16 i + l16
+  const int sw = pswz(l16);              // = pswz of rows w*16 + l16
 #pragma unroll
   for (int st = 0; st < kDownK / 64; ++st) {
     // this wave's DMA for stage st is in once at most the later stages' are outstanding
     const int later = min(3, kDownK / 64 - 1 - st);
-    if (later == 3) wait_vm<12>(); else if (later == 2) wait_vm<8>(); else if (later == 1) wait_vm<4>(); else wait_vm<0>();
+    if (later == 3) wait_vm<6>(); else if (later == 2) wait_vm<4>(); else if (later == 1) wait_vm<2>(); else wait_vm<0>();
     const uint16_t* sp = slot(st);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int kq = st * 2 + h;
-      bf16x8 a[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        a[i] = *reinterpret_cast<const bf16x8*>(sp + (i * 16 + l16) * 64 + (((4 * h + g) ^ sw) << 3));
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(sp + l16 * 64 + (((4 * h + g) ^ sw) << 3));
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const bf16x8 b =
             kQRowMajorK ? *reinterpret_cast<const bf16x8*>(s_q + (j * 16 + l16) * kDownKLd + kq * 32 + 8 * g)
                         : frag_tr(s_q, kDownLd, kq * 32, j * 16, lane);
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b, acc[i][j], 0, 0, 0);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[j], 0, 0, 0);
       }
     }
     // the slot is free again once this stage's fragments are in registers
@@ -198,15 +193,13 @@ __global__ __launch_bounds__(256) void k_rank_down(const uint16_t* __restrict__ 
   // lane holds rows 4*(lane/16)+v of column lane%16 in each 16×16 block
   float* out = part + (int64_t)blockIdx.y * M * r;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int64_t row = m0 + w * 32 + i * 16 + 4 * g + v;
-        const int col = c0 + j * 16 + l16;
-        if (row < M && col < r) out[row * r + col] = acc[i][j][v];
-      }
+    for (int v = 0; v < 4; ++v) {
+      const int64_t row = m0 + w * 16 + 4 * g + v;
+      const int col = c0 + j * 16 + l16;
+      if (row < M && col < r) out[row * r + col] = acc[j][v];
+    }
 }
 
 namespace {
@@ -408,9 +401,9 @@ hipError_t launch_rank_down(bool q_rowmajor_k, const uint16_t* P, int64_t M, int
   dim3 grid((unsigned)((M + kDownRows - 1) / kDownRows), (unsigned)rank_down_splits(K),
             (unsigned)((r + 63) / 64));
   if (q_rowmajor_k)
-    launch(k_rank_down<true>, grid, dim3(256), 0, st, P, M, K, Q, r, part);
+    launch(k_rank_down<true>, grid, dim3(512), 0, st, P, M, K, Q, r, part);
   else
-    launch(k_rank_down<false>, grid, dim3(256), 0, st, P, M, K, Q, r, part);
+    launch(k_rank_down<false>, grid, dim3(512), 0, st, P, M, K, Q, r, part);
   return hipGetLastError();
 }
 
