@@ -203,7 +203,7 @@ __global__ __launch_bounds__(512) void k_rank_down(const uint16_t* __restrict__ 
 }
 
 namespace {
-constexpr int kGradP = 128;       // big-dimension columns per workgroup (4 waves × 32)
+constexpr int kGradP = 128;       // big-dimension columns per workgroup (8 waves × 16)
 constexpr int kGradM = 1024;      // tokens per workgroup (split of the reduction)
 constexpr int kGradChunk = 64;    // tokens per LDS stage
 constexpr int kBigStage = kGradChunk * kGradP;   // bf16 elements of a BIG stage (16 KB)
@@ -237,33 +237,30 @@ __device__ __forceinline__ uint32_t frag_off(int x0, int lane) {
   return (uint32_t)(row * (kBig ? 2 * kGradP : 128) + ((((col >> 3) ^ sw)) << 4) + (col & 7) * 2);
 }
 
-// The twelve transposed reads of one 32-token step: BIG fragments at b0, b1
+// The ten transposed reads of one 32-token step: the BIG fragment at b0
 // (second read +1024 bytes), SMALL fragments at s0..s3 (+512 bytes).  The
 // reads target LDS filled by buffer_load ... lds, so they are issued here
 // with an explicit wait: the block returns with every result in place.
 struct GradFrags {
-  s16x4 b[2][2], s[4][2];
+  s16x4 b[2], s[4][2];
 };
-__device__ __forceinline__ void grad_reads(GradFrags& f, uint32_t b0, uint32_t b1, uint32_t s0,
-                                           uint32_t s1, uint32_t s2, uint32_t s3) {
+__device__ __forceinline__ void grad_reads(GradFrags& f, uint32_t b0, uint32_t s0, uint32_t s1,
+                                           uint32_t s2, uint32_t s3) {
   asm volatile(
-      "ds_read_b64_tr_b16 %0, %12\n\t"
-      "ds_read_b64_tr_b16 %1, %12 offset:1024\n\t"
-      "ds_read_b64_tr_b16 %2, %13\n\t"
-      "ds_read_b64_tr_b16 %3, %13 offset:1024\n\t"
-      "ds_read_b64_tr_b16 %4, %14\n\t"
-      "ds_read_b64_tr_b16 %5, %14 offset:512\n\t"
-      "ds_read_b64_tr_b16 %6, %15\n\t"
-      "ds_read_b64_tr_b16 %7, %15 offset:512\n\t"
-      "ds_read_b64_tr_b16 %8, %16\n\t"
-      "ds_read_b64_tr_b16 %9, %16 offset:512\n\t"
-      "ds_read_b64_tr_b16 %10, %17\n\t"
-      "ds_read_b64_tr_b16 %11, %17 offset:512\n\t"
+      "ds_read_b64_tr_b16 %0, %10\n\t"
+      "ds_read_b64_tr_b16 %1, %10 offset:1024\n\t"
+      "ds_read_b64_tr_b16 %2, %11\n\t"
+      "ds_read_b64_tr_b16 %3, %11 offset:512\n\t"
+      "ds_read_b64_tr_b16 %4, %12\n\t"
+      "ds_read_b64_tr_b16 %5, %12 offset:512\n\t"
+      "ds_read_b64_tr_b16 %6, %13\n\t"
+      "ds_read_b64_tr_b16 %7, %13 offset:512\n\t"
+      "ds_read_b64_tr_b16 %8, %14\n\t"
+      "ds_read_b64_tr_b16 %9, %14 offset:512\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=&v"(f.b[0][0]), "=&v"(f.b[0][1]), "=&v"(f.b[1][0]), "=&v"(f.b[1][1]), "=&v"(f.s[0][0]),
-        "=&v"(f.s[0][1]), "=&v"(f.s[1][0]), "=&v"(f.s[1][1]), "=&v"(f.s[2][0]), "=&v"(f.s[2][1]),
-        "=&v"(f.s[3][0]), "=&v"(f.s[3][1])
-      : "v"(b0), "v"(b1), "v"(s0), "v"(s1), "v"(s2), "v"(s3)
+      : "=&v"(f.b[0]), "=&v"(f.b[1]), "=&v"(f.s[0][0]), "=&v"(f.s[0][1]), "=&v"(f.s[1][0]),
+        "=&v"(f.s[1][1]), "=&v"(f.s[2][0]), "=&v"(f.s[2][1]), "=&v"(f.s[3][0]), "=&v"(f.s[3][1])
+      : "v"(b0), "v"(s0), "v"(s1), "v"(s2), "v"(s3)
       : "memory");
 }
 __device__ __forceinline__ bf16x8 join(const s16x4 (&x)[2]) {
@@ -279,8 +276,10 @@ __device__ __forceinline__ bf16x8 join(const s16x4 (&x)[2]) {
 //
 // BIG [64 tokens][128 p] and SMALL [64 tokens][64 j] stages stream memory ->
 // LDS by buffer_load ... lds (whole cache lines, 1 KB per instruction)
-// through a 3-slot ring, two stages ahead; one LDS barrier per stage.
-__global__ __launch_bounds__(256) void k_rank_grad(RankGradJob ja, RankGradJob jb, int r, int64_t M) {
+// through a 3-slot ring, two stages ahead; one LDS barrier per stage.  8
+// waves of 16 columns p (90 VGPRs): two workgroups per CU, four waves per
+// SIMD.
+__global__ __launch_bounds__(512) void k_rank_grad(RankGradJob ja, RankGradJob jb, int r, int64_t M) {
   __shared__ __attribute__((aligned(16))) uint16_t sb0[kBigStage], sb1[kBigStage], sb2[kBigStage];
   __shared__ __attribute__((aligned(16))) uint16_t ss0[kSmallStage], ss1[kSmallStage], ss2[kSmallStage];
   const int t = threadIdx.x, lane = t & 63;
@@ -301,23 +300,22 @@ __global__ __launch_bounds__(256) void k_rank_grad(RankGradJob ja, RankGradJob j
   auto big_slot = [&](int c) -> uint16_t* { return c % 3 == 0 ? sb0 : c % 3 == 1 ? sb1 : sb2; };
   auto small_slot = [&](int c) -> uint16_t* { return c % 3 == 0 ? ss0 : c % 3 == 1 ? ss1 : ss2; };
   // stage c of the slice (tokens mz + 64 c ..); tokens past M, columns past
-  // P or r read 0.  Wave w moves BIG rows 16w .. 16w+15 and SMALL rows
-  // 16w .. 16w+15.
+  // P or r read 0.  Wave w moves BIG rows 8w .. 8w+7 and SMALL rows
+  // 8w .. 8w+7.
   auto dma = [&](int c) {
     uint16_t* sb = big_slot(c);
     uint16_t* ss = small_slot(c);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {              // 4 rows × 256 bytes per instruction
-      const int q = 4 * w + u, row = 4 * q + (lane >> 4);
+    for (int u = 0; u < 2; ++u) {              // 4 rows × 256 bytes per instruction
+      const int q = 2 * w + u, row = 4 * q + (lane >> 4);
       const int tok = c * kGradChunk + row;
       const int64_t col = p0 + 8 * ((lane & 15) ^ big_swz(row));
       const uint32_t off = (tok < mlen && col < P) ? (uint32_t)((tok * P + col) * 2) : kOob;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rb, (__attribute__((address_space(3))) void*)(sb + q * 512), 16, off, 0, 0, 0);
     }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {              // 8 rows × 128 bytes per instruction
-      const int q = 2 * w + u, row = 8 * q + (lane >> 3);
+    {                                          // 8 rows × 128 bytes per instruction
+      const int q = w, row = 8 * q + (lane >> 3);
       const int tok = c * kGradChunk + row;
       const int col = c0 + 8 * ((lane & 7) ^ small_swz(row));
       const uint32_t off = (tok < mlen && col < r) ? (uint32_t)((tok * r + col) * 2) : kOob;
@@ -329,14 +327,12 @@ __global__ __launch_bounds__(256) void k_rank_grad(RankGradJob ja, RankGradJob j
   // the main loop and the epilogue, for one output layout (uniform per workgroup)
   auto body = [&](auto pj_tag) {
   constexpr bool kOutPJ = decltype(pj_tag)::value;
-  f32x4 acc[2][4];
+  f32x4 acc[4];                          // the wave's 16 columns p × 4 blocks of 16 j
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
   constexpr int kChunks = kGradM / kGradChunk;   // a slice shorter than kGradM streams zero stages
-  const uint32_t ob0 = frag_off<true>(w * 32, lane), ob1 = frag_off<true>(w * 32 + 16, lane);
+  const uint32_t ob0 = frag_off<true>(w * 16, lane);
   const uint32_t os0 = frag_off<false>(0, lane), os1 = frag_off<false>(16, lane);
   const uint32_t os2 = frag_off<false>(32, lane), os3 = frag_off<false>(48, lane);
   dma(0);
@@ -344,7 +340,7 @@ __global__ __launch_bounds__(256) void k_rank_grad(RankGradJob ja, RankGradJob j
 #pragma unroll
   for (int c = 0; c < kChunks; ++c) {
     // this wave's part of stage c is in once at most stage c+1 is outstanding
-    if (c + 1 < kChunks) wait_vm<6>(); else wait_vm<0>();
+    if (c + 1 < kChunks) wait_vm<3>(); else wait_vm<0>();
     // every wave's part has landed and every wave is done with stage c-1
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if (c + 2 < kChunks) dma(c + 2);           // into the slot of stage c-1
@@ -353,41 +349,36 @@ __global__ __launch_bounds__(256) void k_rank_grad(RankGradJob ja, RankGradJob j
     for (int kq = 0; kq < kGradChunk / 32; ++kq) {
       // 32 tokens further: 32 rows of 256 (BIG) or 128 (SMALL) bytes
       GradFrags f;
-      grad_reads(f, ab + ob0 + kq * 8192, ab + ob1 + kq * 8192, as + os0 + kq * 4096,
+      grad_reads(f, ab + ob0 + kq * 8192, as + os0 + kq * 4096,
                  as + os1 + kq * 4096, as + os2 + kq * 4096, as + os3 + kq * 4096);
-      bf16x8 fb[2], fs[4];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) fb[i] = join(f.b[i]);
+      const bf16x8 fb = join(f.b);
+      bf16x8 fs[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) fs[j] = join(f.s[j]);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = kOutPJ ? __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[i], fs[j], acc[i][j], 0, 0, 0)
-                             : __builtin_amdgcn_mfma_f32_16x16x32_bf16(fs[j], fb[i], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < 4; ++j)
+        acc[j] = kOutPJ ? __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb, fs[j], acc[j], 0, 0, 0)
+                        : __builtin_amdgcn_mfma_f32_16x16x32_bf16(fs[j], fb, acc[j], 0, 0, 0);
     }
   }
-  // out_pj: block (i, j) is D[p][j]: lane holds j = lane%16, p rows 4*(lane/16)+v.
-  // else:   block (i, j) is D[j][p]: lane holds p = lane%16, j rows 4*(lane/16)+v.
+  // out_pj: block j is D[p][j]: lane holds j = lane%16, p rows 4*(lane/16)+v.
+  // else:   block j is D[j][p]: lane holds p = lane%16, j rows 4*(lane/16)+v.
   const int g = lane >> 4, l16 = lane & 15;
   float* out = part + (int64_t)blockIdx.y * P * r;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        if (kOutPJ) {
-          const int64_t p = p0 + w * 32 + i * 16 + 4 * g + v;
-          const int jj = c0 + j * 16 + l16;
-          if (p < P && jj < r) out[p * r + jj] = acc[i][j][v];
-        } else {
-          const int64_t p = p0 + w * 32 + i * 16 + l16;
-          const int jj = c0 + j * 16 + 4 * g + v;
-          if (p < P && jj < r) out[(int64_t)jj * P + p] = acc[i][j][v];
-        }
+    for (int v = 0; v < 4; ++v) {
+      if (kOutPJ) {
+        const int64_t p = p0 + w * 16 + 4 * g + v;
+        const int jj = c0 + j * 16 + l16;
+        if (p < P && jj < r) out[p * r + jj] = acc[j][v];
+      } else {
+        const int64_t p = p0 + w * 16 + l16;
+        const int jj = c0 + j * 16 + 4 * g + v;
+        if (p < P && jj < r) out[(int64_t)jj * P + p] = acc[j][v];
       }
+    }
   };
   if (out_pj) body(std::true_type{}); else body(std::false_type{});
 }
@@ -412,7 +403,7 @@ hipError_t launch_rank_grads(RankGradJob a, RankGradJob b, int r, int64_t M, hip
   b.tiles = b.P > 0 ? (int)((b.P + kGradP - 1) / kGradP) : 0;
   if (a.tiles + b.tiles == 0 || r == 0 || M == 0) return hipSuccess;
   dim3 grid((unsigned)(a.tiles + b.tiles), (unsigned)rank_grad_splits(M), (unsigned)((r + 63) / 64));
-  launch(k_rank_grad, grid, dim3(256), 0, st, a, b, r, M);
+  launch(k_rank_grad, grid, dim3(512), 0, st, a, b, r, M);
   return hipGetLastError();
 }
 
