@@ -254,7 +254,7 @@ def test_noalloc_backward_size_limit(L):
         v = _view(o * d)
         return f(A16, A16, None, M, d, ctypes.byref(v), o, A16, A16, r, 2.0, A16, A16, A16, None)
 
-    for M, d, o in ((4096, 11008, 11008), (4096, 8192, 8192), (16384, 4096, 4096)):
+    for M, d, o in ((4096, 11008, 11008), (8192, 8192, 8192), (16384, 4096, 4096)):
         assert qb.qlora_workspace_bytes(qb.QLORA_OP_BWD, M, d, o, 64) > limit
         assert call(M, d, o) == 8
     for M, d, o in ((4096, 4096, 4096), (4096, 4096, 11008), (4096, 11008, 4096),
