@@ -83,6 +83,9 @@ constexpr int kQuantWaves = 8;                                   // waves per gr
 constexpr int kLaneBlocks = kGroup / (kQuantWaves * 8);        // blocks per lane: 4
 
 // Group g of one tensor (a workgroup of 64·kQuantWaves threads).
+// kStream: the launch streams from HBM; its code words are stored with the
+// non-temporal hint (the next reader is another launch, long after).
+template <bool kStream>
 __device__ __forceinline__ void quantize_group(const float* __restrict__ W, int64_t n,
                                                uint8_t* __restrict__ codes,
                                                uint8_t* __restrict__ scale8,
@@ -209,8 +212,8 @@ __device__ __forceinline__ void quantize_group(const float* __restrict__ W, int6
             word = (word & keep) | (0x77777777u & ~keep);
           }
         }
-        // (stores past the code buffer are dropped)
-        __builtin_amdgcn_raw_buffer_store_b32(word, rcod, wi * 4, 0, 0);
+        // (stores past the code buffer are dropped; cache policy 2 = nt)
+        __builtin_amdgcn_raw_buffer_store_b32(word, rcod, wi * 4, 0, kStream ? 2 : 0);
       }
     }
   };
@@ -251,21 +254,22 @@ __device__ __forceinline__ void quantize_group(const float* __restrict__ W, int6
   if (bad && flags != nullptr) flags[0] = flags[0] | 1;
 }
 
-// kWavesPerSimd: the occupancy the registers are fitted to (see the launchers)
-template <int kWavesPerSimd>
+// kWavesPerSimd: the occupancy the registers are fitted to; kStream: the
+// launch streams its input from HBM (see the launchers)
+template <int kWavesPerSimd, bool kStream>
 __global__ __launch_bounds__(64 * kQuantWaves) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd))) void k_quantize(const float* __restrict__ W, int64_t n,
                                                   uint8_t* __restrict__ codes,
                                                   uint8_t* __restrict__ scale8,
                                                   float* __restrict__ scale2,
                                                   int32_t* __restrict__ flags, Codebook cb,
                                                   EncodeGuide eg) {
-  quantize_group(W, n, codes, scale8, scale2, flags, cb, eg, blockIdx.x);
+  quantize_group<kStream>(W, n, codes, scale8, scale2, flags, cb, eg, blockIdx.x);
 }
 
 // Several tensors in one launch: workgroup i quantizes group i - g0 of the
 // last job whose first workgroup g0 is <= i.  The job is picked by a uniform
 // scan with constant indices, so the table stays in kernel-argument memory.
-template <int kWavesPerSimd>
+template <int kWavesPerSimd, bool kStream>
 __global__ __launch_bounds__(64 * kQuantWaves) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd))) void k_quantize_grouped(QuantJobs jobs, int32_t* __restrict__ flags,
                                                           Codebook cb, EncodeGuide eg) {
   const int64_t i = blockIdx.x;
@@ -273,7 +277,7 @@ __global__ __launch_bounds__(64 * kQuantWaves) __attribute__((amdgpu_waves_per_e
 #pragma unroll
   for (int k = 1; k < kMaxQuantJobs; ++k)
     if (k < jobs.count && i >= jobs.j[k].g0) j = jobs.j[k];
-  quantize_group(j.W, j.n, j.codes, j.scale8, j.scale2, flags, cb, eg, i - j.g0);
+  quantize_group<kStream>(j.W, j.n, j.codes, j.scale8, j.scale2, flags, cb, eg, i - j.g0);
 }
 
 // ------------------------------------------------------------------ dequant
@@ -463,7 +467,11 @@ hipError_t launch_dq_variant(const float* W, int64_t n, uint8_t* scale8, float* 
 // HBM runs two (five waves per SIMD: 85 VGPRs), whose fewer, longer bursts
 // stream better.  Measured on one box against two per CU: 4096² 1–9 %
 // faster, 11008×4096 4–5 %, 8192² (268 MB) 1 %; with three per CU
-// 12288×8192 was 7 % and 22016×8192 9 % slower.
+// 12288×8192 was 7 % and 22016×8192 9 % slower.  The streaming launch also
+// stores its code words non-temporally: 22016×8192 4–6 % and 12288×8192 4 %
+// faster, the seven 65B-style tensors 3–5 % (non-temporal loads of W were
+// 12 % slower, non-temporal 8-bit scales no faster, and the hint changed
+// nothing on the shapes that stay in the MALL).
 constexpr int64_t kQuantStreamBytes = 320ll << 20;
 static bool quant_streams(int64_t groups) { return groups * (int64_t)kGroupElems * 4 > kQuantStreamBytes; }
 
@@ -474,10 +482,10 @@ hipError_t launch_quantize(const float* W, int64_t n, uint8_t* codes, uint8_t* s
   const EncodeGuide& eg = host_encode_guide(fmt);
   if (eg.zero_cell < 0) return hipErrorInvalidValue;
   if (quant_streams(ng))
-    launch(k_quantize<5>, dim3((unsigned)ng), dim3(64 * kQuantWaves), 0, st, W, n, codes, scale8, scale2,
+    launch(k_quantize<5, true>, dim3((unsigned)ng), dim3(64 * kQuantWaves), 0, st, W, n, codes, scale8, scale2,
            flags, host_codebook(fmt), eg);
   else
-    launch(k_quantize<6>, dim3((unsigned)ng), dim3(64 * kQuantWaves), 0, st, W, n, codes, scale8, scale2,
+    launch(k_quantize<6, false>, dim3((unsigned)ng), dim3(64 * kQuantWaves), 0, st, W, n, codes, scale8, scale2,
            flags, host_codebook(fmt), eg);
   return hipGetLastError();
 }
@@ -491,10 +499,10 @@ hipError_t launch_quantize_grouped(const QuantJobs& jobs, int32_t* flags, int fm
   const EncodeGuide& eg = host_encode_guide(fmt);
   if (eg.zero_cell < 0) return hipErrorInvalidValue;
   if (quant_streams(groups))
-    launch(k_quantize_grouped<5>, dim3((unsigned)groups), dim3(64 * kQuantWaves), 0, st, jobs, flags,
+    launch(k_quantize_grouped<5, true>, dim3((unsigned)groups), dim3(64 * kQuantWaves), 0, st, jobs, flags,
            host_codebook(fmt), eg);
   else
-    launch(k_quantize_grouped<6>, dim3((unsigned)groups), dim3(64 * kQuantWaves), 0, st, jobs, flags,
+    launch(k_quantize_grouped<6, false>, dim3((unsigned)groups), dim3(64 * kQuantWaves), 0, st, jobs, flags,
            host_codebook(fmt), eg);
   return hipGetLastError();
 }
