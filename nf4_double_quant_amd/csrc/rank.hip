@@ -15,9 +15,14 @@
 //    tokens of one column per read).
 // Split planes are summed in a fixed order (k_reduce_planes, or the tail of
 // the backward dX launch for the dA and dB planes), so results are bitwise
-// reproducible.  (Summing them inside these kernels, with the
-// last workgroup of a tile reducing, costs more on this chip: every
-// device-scope release fence writes back the XCD's whole L2.)
+// reproducible.  (Summing them inside these kernels, with the last
+// workgroup of a row block reducing, costs more on this chip.  With
+// device-scope release fences every workgroup writes back its XCD's whole
+// L2; with planes written through to the device-coherent level and a relaxed
+// count instead, the sums stay bitwise the same, but the last workgroups of
+// the 32 row blocks of a 4096-token product do all of the summing on 32 of
+// the 256 CUs: 20 µs per product against 9 + 4 for the product and
+// k_reduce_planes.)
 #include <type_traits>
 
 #include "kernels.h"
