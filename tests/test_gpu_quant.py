@@ -6,7 +6,8 @@ levels, zero blocks and groups, subnormals, huge magnitudes), weights on a
 fine grid of w/c1 and at the edges of the fp32 range, non-finite
 input, determinism, and the full-size weight shapes of the 4096×4096 layer,
 the 7B-style MLP (11008×4096) and the 65B-style MLP (22016×8192), the last
-two checked on sampled double-quant groups (quantization is group-local).
+two checked on sampled double-quant groups (quantization is group-local),
+and a ragged tensor large enough for the streaming launch configuration.
 """
 
 import numpy as np
@@ -181,3 +182,36 @@ def test_full_size_sampled_groups(wname, proj):
         assert np.array_equal(rs8, s8[g * 256:(g + 1) * 256]), g
         assert np.array_equal(rc, c[g * GE // 2:(g + 1) * GE // 2]), g
     del q
+
+
+def test_streaming_instance_ragged():
+    """A tensor past the size where the quantizer streams from HBM (its other
+    launch configuration, with non-temporal code stores), with a length that
+    ends inside a block and inside a code word: sampled groups and the partial
+    last group against the oracle, alone and as a member of a grouped launch
+    with a small ragged tensor."""
+    n = 84_000_000 + 4097
+    assert n * 4 > 320 << 20
+    W = synth.normal_f32((n,), 0.02, [631, 0])
+    small = synth.normal_f32((3 * GE + 4097,), 0.02, [631, 1])
+    q, c, s8, s2 = gpu_quantize(W)
+    ng = s2.size
+    assert ng == (n + GE - 1) // GE
+    grouped = qb.qlora_quantize_nf4_dq_grouped([torch.from_numpy(W).cuda(), torch.from_numpy(small).cuda()])
+    torch.cuda.synchronize()
+    gc = grouped[0].codes.cpu().numpy()[: c.size]
+    gs8 = grouped[0].scale8.cpu().numpy()[: s8.size]
+    gs2 = grouped[0].scale2.cpu().numpy()[: s2.size]
+    assert np.array_equal(gc, c) and np.array_equal(gs8, s8) and np.array_equal(gs2.view(np.uint32), s2.view(np.uint32))
+    groups = sorted(set(np.random.default_rng(1).choice(ng - 1, 8, replace=False).tolist()) | {0, ng - 1})
+    for g in groups:
+        rc, rs8, rs2 = nf4.quantize(W[g * GE:(g + 1) * GE])
+        assert rs2[0].view(np.uint32) == s2[g].view(np.uint32), g
+        assert np.array_equal(rs8, s8[g * 256: g * 256 + rs8.size]), g
+        assert np.array_equal(rc, c[g * GE // 2: g * GE // 2 + rc.size]), g
+    rc, rs8, rs2 = nf4.quantize(small)
+    got = (grouped[1].codes.cpu().numpy()[: rc.size], grouped[1].scale8.cpu().numpy()[: rs8.size],
+           grouped[1].scale2.cpu().numpy()[: rs2.size])
+    assert np.array_equal(got[0], rc) and np.array_equal(got[1], rs8)
+    assert np.array_equal(got[2].view(np.uint32), np.asarray(rs2, dtype=np.float32).view(np.uint32))
+    del q, grouped
